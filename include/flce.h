@@ -1,0 +1,135 @@
+/*
+ * flce.h - C ABI of the MI355X (gfx950) fused linear + cross-entropy library.
+ *
+ * The operation (fused linear + cross-entropy, FLCE):
+ *   z      = x . W^T                     logits, [N, V], never stored in memory
+ *   lse_i  = log sum_v exp(z_iv)         per-token log-sum-exp
+ *   l_i    = lse_i - z_{i, t_i}          per-token cross-entropy
+ *   loss   = sum_i l_i  (FLCE_SUM)  or  (1/N) sum_i l_i  (FLCE_MEAN)
+ *   D      = s (softmax(z) - onehot(t)), s = grad_loss / N (mean) or grad_loss (sum)
+ *   grad_x = D . W        [N, H]
+ *   grad_W = D^T . x      [V, H]
+ *
+ * Sources (pages on fused linear + cross-entropy):
+ *   - "Fused linear + cross-entropy" (KernelIndex operation page), description and
+ *     Semantics table: x float [tokens, hidden], weight float [vocab, hidden],
+ *     target int64 [tokens], loss float [1]; no mutation or aliasing.
+ *   - "[example] fused_linear_cross_entropy kernel" (pytorch/helion PR #1268), PR
+ *     description: the forward is a tiled matmul with an online softmax that yields
+ *     the log-sum-exp and the target logit and keeps the log-sum-exp for the
+ *     backward; the backward recomputes the logits and accumulates the input and
+ *     weight gradients.
+ *   - "feat(FLCE): add helion version of fused linear cross entropy"
+ *     (linkedin/Liger-Kernel PR #928), test log: reductions sum and mean; ragged
+ *     shapes where out-of-range dlogits must not leak into the weight gradient.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named x, W, target, lse, grad_loss, loss, grad_x, grad_W, ws are
+ *     DEVICE pointers (memory of the current HIP device).  The library never
+ *     allocates, frees or synchronises: the caller owns every buffer, and all work
+ *     is enqueued on `hip_stream` (a hipStream_t passed as void*, NULL = default
+ *     stream).  Outputs are ready when the stream reaches them.
+ *   - Layout: every tensor is contiguous and row-major.  x is [N, H], W is [V, H]
+ *     (the nn.Linear weight layout, hidden contiguous), target is [N] int64.
+ *   - x and W have the element type `dt`; loss, lse and target_logit are float32;
+ *     grad_x and grad_W have the element type `dt` and are overwritten (not
+ *     accumulated into).
+ *   - Inputs are never written.  No output may overlap an input or another output
+ *     (FLCE_ERR_ALIAS), and the workspace may overlap nothing.
+ *   - x and W base pointers must be 16-byte aligned and H * sizeof(dt) must be a
+ *     multiple of 16 (FLCE_ERR_ALIGN otherwise).
+ *   - Targets must lie in [0, V).  The kernels never read out of bounds for other
+ *     values: such a token gets a NaN loss term and no one-hot term in D.
+ *   - A status other than FLCE_OK means nothing was enqueued, except FLCE_ERR_HIP,
+ *     which reports a failed kernel launch.  The library never prints.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x, W, grad_x and grad_W. */
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype;
+
+/* Reduction of the per-token losses (Liger-Kernel PR #928 test matrix: sum, mean). */
+typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1 } flce_reduction;
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  FLCE_ERR_SHAPE = 2,     /* N, H or V <= 0, or a size too large to index         */
+  FLCE_ERR_DTYPE = 3,     /* unknown flce_dtype                                   */
+  FLCE_ERR_REDUCTION = 4, /* unknown flce_reduction                               */
+  FLCE_ERR_ALIAS = 5,     /* an output overlaps an input, another output or ws    */
+  FLCE_ERR_ALIGN = 6,     /* misaligned x/W, or H * sizeof(dt) not a multiple of 16 */
+  FLCE_ERR_WORKSPACE = 7, /* ws is NULL or smaller than required                  */
+  FLCE_ERR_HIP = 8        /* a HIP launch failed                                  */
+} flce_status;
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char* flce_status_string(flce_status status);
+
+/* Bytes of device workspace flce_forward needs for these sizes (a pure function
+ * of its arguments; 0 for invalid arguments). */
+size_t flce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
+
+/*
+ * Forward pass.  Source: helion PR #1268, PR description (tiled matmul plus an
+ * online softmax give the log-sum-exp and the target logit; the log-sum-exp is
+ * kept for the backward); KernelIndex Semantics table (shapes, dtypes).
+ *
+ *   x            [N, H] dt         input activations
+ *   W            [V, H] dt         LM-head weight
+ *   target       [N] int64         class index per token, in [0, V)
+ *   loss         [1] float32       out: sum or mean of the per-token losses
+ *   lse          [N] float32       out: per-token log-sum-exp (input to the backward)
+ *   target_logit [N] float32       out, may be NULL: z_{i, t_i} per token
+ *   ws, ws_bytes                   device workspace, >= flce_forward_workspace_bytes
+ *
+ * The logits are never written to memory.  The result is bitwise reproducible
+ * run to run (fixed reduction order, no atomics).
+ */
+flce_status flce_forward(const void* x, const void* W, const int64_t* target, int64_t N,
+                         int64_t H, int64_t V, flce_dtype dt, flce_reduction reduction,
+                         float* loss, float* lse, float* target_logit, void* ws,
+                         size_t ws_bytes, void* hip_stream);
+
+/* Bytes of device workspace flce_backward needs for these sizes (a pure function
+ * of its arguments; 0 for invalid arguments).  A larger workspace lets the
+ * backward use larger dlogit panels (fewer passes); a smaller one, down to
+ * flce_backward_min_workspace_bytes, makes it use smaller panels. */
+size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
+size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
+
+/*
+ * Backward pass.  Source: helion PR #1268, PR description (the backward
+ * recomputes the logits and accumulates the input and weight gradients);
+ * Liger-Kernel PR #928 (out-of-range dlogit entries must be zero so the weight
+ * gradient never picks up NaN or garbage on ragged shapes).
+ *
+ *   x, W, target, N, H, V, dt, reduction   as for flce_forward (same values)
+ *   lse        [N] float32       the lse written by flce_forward for these inputs
+ *   grad_loss  [1] float32       device scalar: upstream gradient of loss
+ *   grad_x     [N, H] dt         out: D . W
+ *   grad_W     [V, H] dt         out: D^T . x
+ *   ws, ws_bytes                 device workspace, >= flce_backward_min_workspace_bytes
+ *
+ * The logit tiles are recomputed from x and W; the dlogits exist only as
+ * bounded panels inside `ws` (never the N x V matrix).  Deterministic: no
+ * atomics, fixed accumulation order.
+ */
+flce_status flce_backward(const void* x, const void* W, const int64_t* target,
+                          const float* lse, const float* grad_loss, int64_t N, int64_t H,
+                          int64_t V, flce_dtype dt, flce_reduction reduction, void* grad_x,
+                          void* grad_W, void* ws, size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */
