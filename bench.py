@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of fused linear + cross-entropy on one MI355X.
+
+One step = flce_forward + flce_backward (loss, lse, grad_x, grad_W) over the
+Llama-3 head workload (V=128256, H=4096, N=4096 tokens, bf16 inputs, mean),
+inputs resident in HBM.  Prints one JSON line with the throughput (8NHV flop
+per step), forward time, per-kernel timings from HIP events recorded between
+the library's launches, the roofline of the dominant kernel and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd ms & TFLOP/s (8NHV) at V=128256 H=4096 N=4096 bf16; fwd ms"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_4k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, W, t, dtype, H, V, target_s):
+    """Time the CPU oracle (forward, then backward) on a token sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from lm_head_linear_tiled_amd.inputs import widen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas")
+    except Exception:  # threadpoolctl missing: fall back to the affinity mask
+        cores = len(os.sched_getaffinity(0))
+    Wf = widen(W, dtype)
+
+    def run(n):
+        xs = widen(x[:n], dtype)
+        ts = t[:n]
+        t0 = time.perf_counter()
+        oracle.forward(xs, Wf, ts, "mean")
+        oracle.backward(xs, Wf, ts, "mean")
+        return time.perf_counter() - t0
+
+    n, secs = 16, run(16)
+    while secs < target_s / 4 and n < len(t):  # grow the sample until it is timeable
+        n = min(len(t), 4 * n)
+        secs = run(n)
+    if secs < target_s and n < len(t):
+        n = int(min(len(t), n * target_s / secs))
+        secs = run(n)
+    tflops = 8.0 * n * H * V / secs / 1e12
+    return {"value": round(tflops, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {len(t)} tokens x full V={V}, H={H}: oracle.forward then oracle.backward "
+                      f"(float64 numpy, logits materialised per token chunk), {secs:.1f} s",
+            "seconds": round(secs, 2), "tokens": n}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path has no multi-GPU sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from lm_head_linear_tiled_amd import binding, roofline
+    from lm_head_linear_tiled_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    N, H, V, dtype = w.N, w.H, w.V, w.dtype
+    red = "mean"
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x, W, t = make_inputs(N, H, V, dtype, seed=0)
+    if dtype == "bf16":
+        xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        Wd = torch.from_numpy(W.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        xd, Wd = torch.from_numpy(x).to(dev), torch.from_numpy(W).to(dev)
+    td = torch.from_numpy(t).to(dev)
+    gl = torch.ones(1, dtype=torch.float32, device=dev)
+    fws = torch.empty(binding.forward_workspace_bytes(N, H, V, tdt), dtype=torch.uint8, device=dev)
+    bws = torch.empty(binding.backward_workspace_bytes(N, H, V, tdt), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step(ft=None, bt=None):
+        loss, lse = binding.flce_forward(xd, Wd, td, red, workspace=fws, timer=ft)
+        gx, gW = binding.flce_backward(xd, Wd, td, lse, gl, red, workspace=bws, timer=bt)
+        return loss, gx, gW
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_bwd_launches = 3 * 256  # covers every panel and chunk launch at these sizes
+    ftimers = [binding.KernelTimer(4) for _ in range(args.steps)]
+    btimers = [binding.KernelTimer(n_bwd_launches + 1) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for k in range(args.steps):
+        loss, gx, gW = step(ftimers[k], btimers[k])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # forward alone
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record()
+    for _ in range(args.steps):
+        binding.flce_forward(xd, Wd, td, red, workspace=fws)
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    # per-kernel durations from the events recorded inside the timed steps
+    per = {}
+    for tm in ftimers + btimers:
+        for name, ms in tm.durations():
+            per.setdefault(name, []).append(ms)
+    fl_kind = {"fwd_partial": roofline.fwd_flops(N, H, V)}
+    for k in ("bwd_dlogits", "bwd_grad_w", "bwd_grad_x"):
+        fl_kind[k] = roofline.fwd_flops(N, H, V)  # each backward contraction sums to 2NHV over a step
+    kernels = {}
+    for name, ms in per.items():
+        tot = sum(ms) / args.steps
+        kernels[name] = {"launches_per_step": len(ms) // args.steps, "avg_ms": round(sum(ms) / len(ms), 4),
+                         "ms_per_step": round(tot, 4)}
+        if name in fl_kind:
+            kernels[name]["tflops"] = round(fl_kind[name] / (tot * 1e-3) / 1e12, 2)
+    dom = max((k for k in kernels if k in fl_kind), key=lambda k: kernels[k]["ms_per_step"])
+    launches = kernels[dom]["launches_per_step"]
+    flops_per_launch = fl_kind[dom] / launches
+    achieved = flops_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+    peak = roofline.PEAK_TFLOPS[dtype]
+
+    total_flops = roofline.fwdbwd_flops(N, H, V)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (x~N(0,1), W~N(0,1/sqrt(H)), targets uniform, seed 0)",
+        "config": {"workload": f"llama3 head V={V} H={H} N={N} {dtype} mean, forward+backward",
+                   "N": N, "H": H, "V": V, "reduction": red},
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(roofline.fwd_flops(N, H, V) / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwdbwd_frac_of_peak": round(value / peak, 4),
+        "fwd_frac_of_peak": round(roofline.fwd_flops(N, H, V) / (fwd_ms * 1e-3) / 1e12 / peak, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "peak_mem_bytes": int(peak_mem),
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "flops_per_launch": flops_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, W, t, dtype, H, V, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -128,6 +128,42 @@ flce_status flce_backward(const void* x, const void* W, const int64_t* target,
                           int64_t V, flce_dtype dt, flce_reduction reduction, void* grad_x,
                           void* grad_W, void* ws, size_t ws_bytes, void* hip_stream);
 
+/*
+ * Kernel timing, for benchmarks: the *_timed variants behave exactly like the
+ * calls above and, in addition, record caller-created HIP events (hipEvent_t
+ * handles passed as void*) on `hip_stream`: events[0] before the first kernel and
+ * events[k + 1] right after kernel k, for the first n_events - 1 kernels.  kinds[k]
+ * receives the flce_kernel of launch k, n_launches the number of kernels enqueued
+ * (also those beyond the event capacity).  `timing` may be NULL.  A failed event
+ * record is reported as FLCE_ERR_HIP.
+ */
+typedef enum {
+  FLCE_K_FWD_PARTIAL = 0, /* logit tiles + online (max, sum-exp) per vocabulary split */
+  FLCE_K_FWD_COMBINE = 1, /* split merge -> lse, per-token loss, block sums          */
+  FLCE_K_FWD_LOSS = 2,    /* block sums -> scalar loss                             */
+  FLCE_K_BWD_DLOGITS = 3, /* logit tile recompute -> dlogit panel                   */
+  FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
+  FLCE_K_BWD_GRAD_X = 5   /* grad_x rows of one token chunk, one panel              */
+} flce_kernel;
+
+typedef struct {
+  void* const* events; /* in: hipEvent_t handles                          */
+  int n_events;        /* in: number of handles                           */
+  int* kinds;          /* out: flce_kernel per launch, >= n_events - 1     */
+  int n_launches;      /* out: kernels enqueued by the call                */
+} flce_timing;
+
+flce_status flce_forward_timed(const void* x, const void* W, const int64_t* target, int64_t N,
+                               int64_t H, int64_t V, flce_dtype dt, flce_reduction reduction,
+                               float* loss, float* lse, float* target_logit, void* ws,
+                               size_t ws_bytes, void* hip_stream, flce_timing* timing);
+
+flce_status flce_backward_timed(const void* x, const void* W, const int64_t* target,
+                                const float* lse, const float* grad_loss, int64_t N, int64_t H,
+                                int64_t V, flce_dtype dt, flce_reduction reduction, void* grad_x,
+                                void* grad_W, void* ws, size_t ws_bytes, void* hip_stream,
+                                flce_timing* timing);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,240 @@
+// Host layer of the fused linear + cross-entropy library: the C ABI declared in
+// include/flce.h.  Every argument is checked here, before any HIP call, so that
+// a bad call enqueues nothing; then the launch plan is drawn up, the caller's
+// workspace is carved, and the kernels are enqueued on the caller's stream.
+#include "flce.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "flce_launch.h"
+
+namespace {
+
+using flce::BwdPlan;
+using flce::FwdPlan;
+using flce::kTile;
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;     // keeps every int index in range
+constexpr int kFwdTargetWorkgroups = 2048;         // 8 per CU on a 256-CU part
+constexpr size_t kDefaultPanelBytes = 64u << 20;   // dlogit panel budget
+constexpr int kMinVocabPerPanel = 2048;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t esize(flce_dtype dt) { return dt == FLCE_BF16 ? 2 : 4; }
+
+bool dims_ok(int64_t N, int64_t H, int64_t V) {
+  return N > 0 && H > 0 && V > 0 && N <= kMaxDim && H <= kMaxDim && V <= kMaxDim;
+}
+bool dtype_ok(flce_dtype dt) { return dt == FLCE_F32 || dt == FLCE_BF16; }
+
+FwdPlan plan_forward(int64_t N, int64_t V) {
+  FwdPlan p{};
+  p.tiles_tok = (int)ceil_div(N, kTile);
+  p.Np = p.tiles_tok * kTile;
+  const int tiles_v = (int)ceil_div(V, kTile);
+  int splits = (int)std::min<int64_t>(tiles_v, std::max<int64_t>(1, ceil_div(kFwdTargetWorkgroups, p.tiles_tok)));
+  p.tiles_per_split = (int)ceil_div(tiles_v, splits);
+  p.splits = (int)ceil_div(tiles_v, p.tiles_per_split);  // no empty split
+  size_t o = 0;
+  p.off_m = o;
+  o = align_up(o + sizeof(float) * (size_t)p.splits * p.Np, 256);
+  p.off_s = o;
+  o = align_up(o + sizeof(float) * (size_t)p.splits * p.Np, 256);
+  p.off_zt = o;
+  o = align_up(o + sizeof(float) * (size_t)p.Np, 256);
+  p.off_blk = o;
+  o = align_up(o + sizeof(double) * (size_t)ceil_div(N, 256), 256);
+  p.total = o;
+  return p;
+}
+
+// Dlogit panel of Nc tokens x Vb vocabulary entries holding at most panel_elems
+// values; accumulators only where a gradient is summed over several launches.
+BwdPlan plan_backward_for(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t panel_elems) {
+  BwdPlan p{};
+  const int64_t Np = ceil_div(N, kTile) * kTile;
+  const int64_t Vp = ceil_div(V, kTile) * kTile;
+  int64_t Nc;
+  if (Np * std::min<int64_t>(Vp, kMinVocabPerPanel) <= panel_elems) {
+    Nc = Np;
+  } else {
+    Nc = std::max<int64_t>(kTile, (int64_t)std::sqrt((double)panel_elems) / kTile * kTile);
+    Nc = std::min(Nc, Np);
+  }
+  int64_t Vb = std::max<int64_t>(kTile, panel_elems / Nc / kTile * kTile);
+  Vb = std::min(Vb, Vp);
+  p.Nc = (int)Nc;
+  p.Ncp = (int)Nc;  // a multiple of kTile
+  p.n_chunks = (int)ceil_div(N, Nc);
+  p.Vb = (int)Vb;
+  p.Vbp = (int)Vb;  // a multiple of kTile
+  p.n_panels = (int)ceil_div(V, Vb);
+  const size_t es = esize(dt);
+  // float32 gradients accumulate in place; bfloat16 ones through float32 buffers.
+  p.gx_bytes = (dt == FLCE_BF16 && p.n_panels > 1) ? sizeof(float) * (size_t)N * H : 0;
+  p.gw_bytes = (dt == FLCE_BF16 && p.n_chunks > 1) ? sizeof(float) * (size_t)Vb * H : 0;
+  size_t o = 0;
+  p.off_panel = o;
+  o = align_up(o + es * (size_t)p.Ncp * p.Vbp, 256);
+  p.off_gx = o;
+  o = align_up(o + p.gx_bytes, 256);
+  p.off_gw = o;
+  o = align_up(o + p.gw_bytes, 256);
+  p.total = o;
+  return p;
+}
+
+// Largest panel (up to the default budget) whose plan fits in ws_bytes.
+bool plan_backward(int64_t N, int64_t H, int64_t V, flce_dtype dt, size_t ws_bytes, BwdPlan* out) {
+  int64_t elems = (int64_t)(kDefaultPanelBytes / esize(dt));
+  const int64_t min_elems = int64_t(kTile) * kTile;
+  while (true) {
+    BwdPlan p = plan_backward_for(N, H, V, dt, elems);
+    if (p.total <= ws_bytes) {
+      *out = p;
+      return true;
+    }
+    if (elems <= min_elems) return false;
+    elems = std::max(min_elems, elems / 2);
+  }
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+// Does any output overlap an input, another output or the workspace?
+bool any_alias(const Range* in, int nin, const Range* out, int nout, Range ws) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(out[i], in[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return true;
+    if (overlap(out[i], ws)) return true;
+  }
+  for (int j = 0; j < nin; ++j)
+    if (overlap(ws, in[j])) return true;
+  return false;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+flce_status check_common(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H, int64_t V,
+                         flce_dtype dt, flce_reduction reduction) {
+  if (!x || !W || !target) return FLCE_ERR_NULL;
+  if (!dims_ok(N, H, V)) return FLCE_ERR_SHAPE;
+  if (!dtype_ok(dt)) return FLCE_ERR_DTYPE;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_REDUCTION;
+  if (!aligned16(x) || !aligned16(W) || (H * (int64_t)esize(dt)) % 16 != 0) return FLCE_ERR_ALIGN;
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_string(flce_status s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_NULL: return "FLCE_ERR_NULL: a required pointer is NULL";
+    case FLCE_ERR_SHAPE: return "FLCE_ERR_SHAPE: N, H and V must lie in [1, 2^30]";
+    case FLCE_ERR_DTYPE: return "FLCE_ERR_DTYPE: unknown element type";
+    case FLCE_ERR_REDUCTION: return "FLCE_ERR_REDUCTION: unknown reduction";
+    case FLCE_ERR_ALIAS: return "FLCE_ERR_ALIAS: an output overlaps an input, another output or the workspace";
+    case FLCE_ERR_ALIGN: return "FLCE_ERR_ALIGN: x and W must be 16-byte aligned and H * sizeof(dtype) a multiple of 16";
+    case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace missing or too small";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP: a HIP kernel launch failed";
+  }
+  return "FLCE: unknown status";
+}
+
+size_t flce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  return plan_forward(N, V).total;
+}
+
+size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  return plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total;
+}
+
+size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  return plan_backward_for(N, H, V, dt, int64_t(kTile) * kTile).total;
+}
+
+flce_status flce_forward(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H, int64_t V,
+                         flce_dtype dt, flce_reduction reduction, float* loss, float* lse, float* target_logit,
+                         void* ws, size_t ws_bytes, void* hip_stream) {
+  return flce_forward_timed(x, W, target, N, H, V, dt, reduction, loss, lse, target_logit, ws, ws_bytes, hip_stream,
+                            nullptr);
+}
+
+flce_status flce_forward_timed(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H, int64_t V,
+                               flce_dtype dt, flce_reduction reduction, float* loss, float* lse, float* target_logit,
+                               void* ws, size_t ws_bytes, void* hip_stream, flce_timing* timing) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (!loss || !lse) return FLCE_ERR_NULL;
+  const FwdPlan p = plan_forward(N, V);
+  const size_t es = esize(dt);
+  const Range in[3] = {{x, (size_t)N * H * es}, {W, (size_t)V * H * es}, {target, 8 * (size_t)N}};
+  const Range out[3] = {{loss, 4}, {lse, 4 * (size_t)N}, {target_logit, 4 * (size_t)N}};
+  if (any_alias(in, 3, out, 3, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
+  if (!ws || ws_bytes < p.total) return FLCE_ERR_WORKSPACE;
+
+  char* base = (char*)ws;
+  float* zt = target_logit ? target_logit : (float*)(base + p.off_zt);
+  const double scale = reduction == FLCE_MEAN ? 1.0 / (double)N : 1.0;
+  flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  hipError_t e = flce::launch_forward((int)dt, p, x, W, target, (int)N, (int)H, (int)V, (float*)(base + p.off_m),
+                                      (float*)(base + p.off_s), zt, lse, (double*)(base + p.off_blk), scale, loss,
+                                      (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+flce_status flce_backward(const void* x, const void* W, const int64_t* target, const float* lse,
+                          const float* grad_loss, int64_t N, int64_t H, int64_t V, flce_dtype dt,
+                          flce_reduction reduction, void* grad_x, void* grad_W, void* ws, size_t ws_bytes,
+                          void* hip_stream) {
+  return flce_backward_timed(x, W, target, lse, grad_loss, N, H, V, dt, reduction, grad_x, grad_W, ws, ws_bytes,
+                             hip_stream, nullptr);
+}
+
+flce_status flce_backward_timed(const void* x, const void* W, const int64_t* target, const float* lse,
+                                const float* grad_loss, int64_t N, int64_t H, int64_t V, flce_dtype dt,
+                                flce_reduction reduction, void* grad_x, void* grad_W, void* ws, size_t ws_bytes,
+                                void* hip_stream, flce_timing* timing) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (!lse || !grad_loss || !grad_x || !grad_W) return FLCE_ERR_NULL;
+  const size_t es = esize(dt);
+  const Range in[5] = {{x, (size_t)N * H * es},
+                       {W, (size_t)V * H * es},
+                       {target, 8 * (size_t)N},
+                       {lse, 4 * (size_t)N},
+                       {grad_loss, 4}};
+  const Range out[2] = {{grad_x, (size_t)N * H * es}, {grad_W, (size_t)V * H * es}};
+  if (any_alias(in, 5, out, 2, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
+  BwdPlan p;
+  if (!ws || !plan_backward(N, H, V, dt, ws_bytes, &p)) return FLCE_ERR_WORKSPACE;
+
+  char* base = (char*)ws;
+  const float red_scale = reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f;
+  flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
+                                       grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
+                                       (float*)(base + p.off_gw), (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+}  // extern "C"

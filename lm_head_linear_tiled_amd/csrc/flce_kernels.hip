@@ -1,0 +1,423 @@
+// HIP kernels of fused linear + cross-entropy for gfx950.
+//
+// Forward (helion PR #1268, PR description: tiled matmul plus online softmax for
+// the log-sum-exp and the target logit; the log-sum-exp is kept):
+//   fwd_partial   one workgroup per (token tile, vocabulary split); for each
+//                 vocabulary tile of its split it forms the logit tile
+//                 S^T = W_tile . x_tile^T with MFMA and folds it into a running
+//                 (max, sum of exp) per token held in registers; the target logit
+//                 is picked out of the one tile that holds it.  The split exists so
+//                 that small token counts still fill all 256 CUs (Liger-Kernel PR
+//                 #928 thread: fusing the logits and the softmax leaves too little
+//                 parallelism at small shapes).
+//   fwd_combine   merges the split partials into lse and the per-token loss, then
+//                 reduces the losses per block in a fixed order.
+//   fwd_loss      sums the block partials in a fixed order into the scalar loss.
+// Backward (helion PR #1268: the backward recomputes the logits; the dlogits
+// drive both gradients; Liger-Kernel PR #928: zero the out-of-range dlogits):
+//   bwd_dlogits   recomputes a logit tile S = x_tile . W_tile^T and writes
+//                 D = s (exp(S - lse) - onehot) into a bounded panel, exactly 0
+//                 outside i < N, v < V;
+//   bwd_grad_w    grad_W[v, h] (+)= sum_i D[i, v] x[i, h] over the panel's tokens;
+//   bwd_grad_x    grad_x[i, h] (+)= sum_v D[i, v] W[v, h] over the panel's vocabulary.
+#include "gemm_core.h"
+#include "flce_launch.h"
+
+namespace flce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Cfg;
+template <>
+struct Cfg<bf16_t> {
+  static constexpr int BK = 64;
+};
+template <>
+struct Cfg<float> {
+  static constexpr int BK = 32;
+};
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void fwd_partial(const T* __restrict__ x, const T* __restrict__ W,
+                                                   const int64_t* __restrict__ target, int N, int H, int V,
+                                                   int tiles_tok, int tiles_per_split, int Np,
+                                                   float* __restrict__ part_m, float* __restrict__ part_s,
+                                                   float* __restrict__ zt_out) {
+  // S^T tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major).
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR> G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+
+  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
+  const int split = lid / tiles_tok, tt = lid % tiles_tok;
+  const int n0 = tt * kTile;
+  const int tiles_v = (V + kTile - 1) / kTile;
+  const int vt_begin = split * tiles_per_split;
+  const int vt_end = min(tiles_v, vt_begin + tiles_per_split);
+
+  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  const Operand<T> A{W, H, V, H};
+  const Operand<T> B{x, H, N, H};
+
+  float mrun[G::FN], srun[G::FN];
+  int tgt[G::FN];
+#pragma unroll
+  for (int j = 0; j < G::FN; ++j) {
+    mrun[j] = -INFINITY;
+    srun[j] = 0.f;
+    const int tok = n0 + wn * G::WN + j * 32 + (l & 31);
+    tgt[j] = tok < N ? (int)min<int64_t>(max<int64_t>(target[tok], -1), (int64_t)V) : -1;
+  }
+
+  typename G::Acc acc;
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int m0 = vt * kTile;
+    G::run(A, B, m0, n0, H, lds, acc);
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+          const float val = v < V ? acc[i][j][r] * kLog2e : -INFINITY;
+          tmax = fmaxf(tmax, val);
+        }
+      const float mnew = fmaxf(mrun[j], tmax);
+      if (mnew != -INFINITY) {
+        float ssum = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+            ssum += v < V ? __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - mnew) : 0.f;
+          }
+        srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - mnew) + ssum;
+        mrun[j] = mnew;
+      }
+      // Target logit: exactly one lane of one workgroup holds (t, tok).
+#pragma unroll
+      for (int i = 0; i < G::FM; ++i) {
+        const int local = tgt[j] - (m0 + wm * G::WM + i * 32);
+        if (local >= 0 && local < 32 && ((local >> 2) & 1) == (l >> 5)) {
+          const int rr = (local >> 3) * 4 + (local & 3);
+          float z = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z = r == rr ? acc[i][j][r] : z;
+          zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = z;
+        }
+      }
+    }
+  }
+
+  // Merge the two lane halves (same token, different vocabulary rows) ...
+#pragma unroll
+  for (int j = 0; j < G::FN; ++j) {
+    const float mo = __shfl_xor(mrun[j], 32);
+    const float so = __shfl_xor(srun[j], 32);
+    const float M = fmaxf(mrun[j], mo);
+    if (M != -INFINITY) {
+      srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - M) + so * __builtin_amdgcn_exp2f(mo - M);
+      mrun[j] = M;
+    }
+  }
+  // ... then the two waves that share the token columns.
+  float* sm = reinterpret_cast<float*>(lds);  // [2][WN] max, then [2][WN] sum
+  if (wm == 1 && l < 32) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      sm[wn * G::WN + j * 32 + l] = mrun[j];
+      sm[2 * G::WN + wn * G::WN + j * 32 + l] = srun[j];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && l < 32) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const float mo = sm[wn * G::WN + j * 32 + l];
+      const float so = sm[2 * G::WN + wn * G::WN + j * 32 + l];
+      const float M = fmaxf(mrun[j], mo);
+      float S = 0.f;
+      if (M != -INFINITY) S = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - M) + so * __builtin_amdgcn_exp2f(mo - M);
+      const int tok = n0 + wn * G::WN + j * 32 + l;
+      if (tok < N) {
+        part_m[(int64_t)split * Np + tok] = M;
+        part_s[(int64_t)split * Np + tok] = S;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ part_m,
+                                                   const float* __restrict__ part_s, int splits, int Np, int N,
+                                                   int V, const int64_t* __restrict__ target,
+                                                   float* __restrict__ zt, float* __restrict__ lse,
+                                                   double* __restrict__ block_loss) {
+  __shared__ double red[256];
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  double li = 0.0;
+  if (i < N) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_m[(int64_t)s * Np + i]);
+    float S = 0.f;
+    for (int s = 0; s < splits; ++s) S += part_s[(int64_t)s * Np + i] * exp2f(part_m[(int64_t)s * Np + i] - M);
+    const float l2 = M + log2f(S);
+    const float lsei = l2 * kLn2;
+    lse[i] = lsei;
+    const int64_t t = target[i];
+    float z = zt[i];
+    if (t < 0 || t >= V) {
+      z = __int_as_float(0x7fc00000);
+      zt[i] = z;
+    }
+    li = (double)lsei - (double)z;
+  }
+  red[threadIdx.x] = li;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_loss[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block_loss, int nb, double scale,
+                                                float* __restrict__ loss) {
+  __shared__ double red[256];
+  double a = 0.0;
+  for (int b = (int)threadIdx.x; b < nb; b += 256) a += block_loss[b];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(red[0] * scale);
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
+                                                   const int64_t* __restrict__ target,
+                                                   const float* __restrict__ lse,
+                                                   const float* __restrict__ grad_loss, float red_scale, int N,
+                                                   int H, int V, int i0, int v0, int tiles_m, int Vbp,
+                                                   T* __restrict__ panel) {
+  // S tile: rows = tokens (A = x, K-major), cols = vocabulary (B = W, K-major).
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR> G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
+  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  const int m0 = i0 + tm * kTile, n0 = v0 + tn * kTile;
+  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  const Operand<T> A{x, H, N, H};
+  const Operand<T> B{W, H, V, H};
+  typename G::Acc acc;
+  G::run(A, B, m0, n0, H, lds, acc);
+
+  const float s = grad_loss[0] * red_scale;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+      const bool rv = row < N;
+      const float lr = rv ? lse[row] * kLog2e : 0.f;
+      const int64_t tr = rv ? target[row] : -1;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        const int col = n0 + wn * G::WN + j * 32 + (l & 31);
+        float d = 0.f;
+        if (rv && col < V) {
+          const float p = __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - lr);
+          d = s * (p - (col == tr ? 1.f : 0.f));
+        }
+        panel[(int64_t)(row - i0) * Vbp + (col - v0)] = from_f32<T>(d);
+      }
+    }
+}
+
+// grad_W[v0 + m, h] for m in the panel: A = panel as [k = token][m = vocab]
+// (MN-major), B = x rows i0.. as [k = token][n = hidden] (MN-major).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
+                                                  const T* __restrict__ x, int H, int V, int i0, int v0,
+                                                  int Vb, int tiles_m, T* __restrict__ gw_out,
+                                                  float* __restrict__ gw_acc, int accumulate, int final) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR> G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
+  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  const Operand<T> A{panel, Vbp, Vbp, Kc};
+  const Operand<T> B{x + (int64_t)i0 * H, H, H, Kc};
+  typename G::Acc acc;
+  G::run(A, B, m0, n0, Kc, lds, acc);
+
+  // gw_out and gw_acc point at row v0 of their buffers; rows are panel-local.
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+      if (m >= Vb || v0 + m >= V) continue;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        const int h = n0 + wn * G::WN + j * 32 + (l & 31);
+        if (h >= H) continue;
+        const int64_t o = (int64_t)m * H + h;
+        float val = acc[i][j][r];
+        if (accumulate) val += gw_acc[o];
+        if (final)
+          gw_out[o] = from_f32<T>(val);
+        else
+          gw_acc[o] = val;
+      }
+    }
+}
+
+// grad_x[i0 + m, h]: A = panel as [m = token][k = vocab] (K-major), B = W rows
+// v0.. as [k = vocab][n = hidden] (MN-major).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
+                                                  const T* __restrict__ W, int H, int N, int i0, int v0,
+                                                  int tiles_m, T* __restrict__ gx_out, float* __restrict__ gx_acc,
+                                                  int accumulate, int final) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR> G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
+  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  const Operand<T> A{panel, Vbp, Kc, Vbp};
+  const Operand<T> B{W + (int64_t)v0 * H, H, H, Kv};
+  typename G::Acc acc;
+  G::run(A, B, m0, n0, Kv, lds, acc);
+
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+      if (m >= Kc) continue;
+      const int row = i0 + m;
+      if (row >= N) continue;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+        const int h = n0 + wn * G::WN + j * 32 + (l & 31);
+        if (h >= H) continue;
+        const int64_t o = (int64_t)row * H + h;
+        float val = acc[i][j][r];
+        if (accumulate) val += gx_acc[o];
+        if (final)
+          gx_out[o] = from_f32<T>(val);
+        else
+          gx_acc[o] = val;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (host side)
+// ---------------------------------------------------------------------------
+template <typename T>
+static hipError_t launch_fwd_t(const FwdPlan& p, const void* x, const void* W, const int64_t* target, int N,
+                               int H, int V, float* part_m, float* part_s, float* zt, float* lse, double* block_loss,
+                               double scale, float* loss, hipStream_t st, Recorder& rec) {
+  const int grid = p.tiles_tok * p.splits;
+  rec.start();
+  hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(256), 0, st, (const T*)x, (const T*)W, target, N, H, V,
+                     p.tiles_tok, p.tiles_per_split, p.Np, part_m, part_s, zt);
+  rec.after(FLCE_K_FWD_PARTIAL);
+  const int nb = (N + 255) / 256;
+  hipLaunchKernelGGL(fwd_combine, dim3(nb), dim3(256), 0, st, part_m, part_s, p.splits, p.Np, N, V, target, zt, lse,
+                     block_loss);
+  rec.after(FLCE_K_FWD_COMBINE);
+  hipLaunchKernelGGL(fwd_loss, dim3(1), dim3(256), 0, st, block_loss, nb, scale, loss);
+  rec.after(FLCE_K_FWD_LOSS);
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : rec.err;
+}
+
+hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W, const int64_t* target, int N,
+                          int H, int V, float* part_m, float* part_s, float* zt, float* lse, double* block_loss,
+                          double scale, float* loss, hipStream_t st, Recorder& rec) {
+  return dt == 1 ? launch_fwd_t<bf16_t>(p, x, W, target, N, H, V, part_m, part_s, zt, lse, block_loss, scale, loss, st,
+                                        rec)
+                 : launch_fwd_t<float>(p, x, W, target, N, H, V, part_m, part_s, zt, lse, block_loss, scale, loss, st,
+                                       rec);
+}
+
+template <typename T>
+static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv, const int64_t* target,
+                               const float* lse, const float* grad_loss, float red_scale, int N, int H, int V,
+                               void* gxv, void* gwv, void* panelv, float* gx_acc, float* gw_acc, hipStream_t st,
+                               Recorder& rec) {
+  const T* x = (const T*)xv;
+  const T* W = (const T*)Wv;
+  T* gx = (T*)gxv;
+  T* gw = (T*)gwv;
+  T* panel = (T*)panelv;
+  const bool f32 = sizeof(T) == 4;
+  // Accumulate float32 outputs in place; bfloat16 outputs go through float32 buffers.
+  float* gxa = f32 ? (float*)gxv : gx_acc;  // [N, H]
+  float* gwa0 = f32 ? (float*)gwv : gw_acc;  // [V, H] in place, or one panel [Vb, H]
+  const int tiles_h = (H + kTile - 1) / kTile;
+  rec.start();
+  for (int pv = 0; pv < p.n_panels; ++pv) {
+    const int v0 = pv * p.Vb;
+    const int Kv = min(p.Vb, V - v0);
+    const int Vbp = p.Vbp;
+    for (int c = 0; c < p.n_chunks; ++c) {
+      const int i0 = c * p.Nc;
+      const int Kc = min(p.Nc, N - i0);
+      const int tiles_m = (Kc + kTile - 1) / kTile;
+      const int tiles_n = (Kv + kTile - 1) / kTile;
+      hipLaunchKernelGGL(bwd_dlogits<T>, dim3(tiles_m * tiles_n), dim3(256), 0, st, x, W, target, lse, grad_loss,
+                         red_scale, N, H, V, i0, v0, tiles_m, Vbp, panel);
+      rec.after(FLCE_K_BWD_DLOGITS);
+      // grad_W rows of this panel accumulate over token chunks.
+      const int gw_tiles_m = tiles_n;
+      float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
+      hipLaunchKernelGGL(bwd_grad_w<T>, dim3(gw_tiles_m * tiles_h), dim3(256), 0, st, (const T*)panel, Vbp, Kc, x, H,
+                         V, i0, v0, Kv, gw_tiles_m, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
+                         c == p.n_chunks - 1 ? 1 : 0);
+      rec.after(FLCE_K_BWD_GRAD_W);
+      // grad_x rows of this chunk accumulate over vocabulary panels.
+      hipLaunchKernelGGL(bwd_grad_x<T>, dim3(tiles_m * tiles_h), dim3(256), 0, st, (const T*)panel, Vbp, Kc, Kv, W, H,
+                         N, i0, v0, tiles_m, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
+      rec.after(FLCE_K_BWD_GRAD_X);
+    }
+  }
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : rec.err;
+}
+
+hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
+                           const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, hipStream_t st,
+                           Recorder& rec) {
+  return dt == 1 ? launch_bwd_t<bf16_t>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
+                                        gw_acc, st, rec)
+                 : launch_bwd_t<float>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
+                                       gw_acc, st, rec);
+}
+
+}  // namespace flce

@@ -1,0 +1,65 @@
+// Internal interface between the host layer (argument checks, planning,
+// workspace carving) and the kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "flce.h"
+
+namespace flce {
+
+constexpr int kTile = 128;  // square output tile of every contraction kernel
+
+struct FwdPlan {
+  int tiles_tok;        // token tiles of kTile
+  int splits;           // vocabulary splits (workgroups per token tile)
+  int tiles_per_split;  // vocabulary tiles per split
+  int Np;               // tiles_tok * kTile
+  size_t off_m, off_s, off_zt, off_blk, total;  // workspace carving (bytes)
+};
+
+struct BwdPlan {
+  int Nc, n_chunks;         // tokens per chunk, chunks
+  int Vb, Vbp, n_panels;    // vocabulary per panel, padded, panels
+  int Ncp;                  // Nc padded to kTile
+  size_t off_panel, off_gx, off_gw, total;  // workspace carving (bytes); 0-sized parts unused
+  size_t gx_bytes, gw_bytes;
+};
+
+// Records the caller's timing events between kernel launches (no-op without one).
+struct Recorder {
+  flce_timing* t;
+  hipStream_t s;
+  hipError_t err;
+  void start() {
+    if (t) {
+      t->n_launches = 0;
+      if (t->n_events > 0) record(t->events[0]);
+    }
+  }
+  void after(int kind) {
+    if (!t) return;
+    const int k = t->n_launches++;
+    if (k + 1 < t->n_events) {
+      if (t->kinds) t->kinds[k] = kind;
+      record(t->events[k + 1]);
+    }
+  }
+  void record(void* ev) {
+    const hipError_t e = hipEventRecord((hipEvent_t)ev, s);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+  }
+};
+
+hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W, const int64_t* target, int N,
+                          int H, int V, float* part_m, float* part_s, float* zt, float* lse, double* block_loss,
+                          double scale, float* loss, hipStream_t st, Recorder& rec);
+
+hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
+                           const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, hipStream_t st,
+                           Recorder& rec);
+
+}  // namespace flce

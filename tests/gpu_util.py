@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU tests: device transfer, a run of the HIP path through
+the C ABI, and the parity bar."""
+import sys
+
+import numpy as np
+import torch
+
+TOL = {
+    # fp32 inputs: loss relative 1e-5, gradients elementwise |d| <= 1e-4 + 1e-4 |ref|
+    "f32": dict(loss_rel=1e-5, g_atol=1e-4, g_rtol=1e-4, lse_atol=2e-5),
+    # bf16 inputs, fp32 accumulation: loss relative 2e-3, gradients max|d| / max|ref| <= 1e-2
+    "bf16": dict(loss_rel=2e-3, g_norm=1e-2, lse_atol=2e-4),
+}
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def to_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_hip(binding, x, W, t, dtype, reduction, grad_loss=1.0, bwd_ws_bytes=None):
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(np.asarray(t, dtype=np.int64)).cuda()
+    loss, lse, zt = binding.flce_forward(xd, Wd, td, reduction, with_target_logit=True)
+    gl = torch.tensor([grad_loss], dtype=torch.float32, device="cuda")
+    ws = None
+    if bwd_ws_bytes is not None:
+        ws = torch.empty(bwd_ws_bytes, dtype=torch.uint8, device="cuda")
+    gx, gW = binding.flce_backward(xd, Wd, td, lse, gl, reduction, workspace=ws)
+    torch.cuda.synchronize()
+    return dict(loss=float(loss.item()), lse=to_f64(lse), zt=to_f64(zt), gx=to_f64(gx), gW=to_f64(gW),
+                raw=dict(loss=loss, lse=lse, zt=zt, gx=gx, gW=gW))
+
+
+def assert_grad_close(got, ref, dtype, name):
+    tol = TOL[dtype]
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if dtype == "f32":
+        err = np.abs(got - ref) - (tol["g_atol"] + tol["g_rtol"] * np.abs(ref))
+        worst = np.unravel_index(np.argmax(err), err.shape)
+        assert err.max() <= 0, f"{name}: |d| {abs(got[worst] - ref[worst]):.3e} at {worst}, ref {ref[worst]:.3e}"
+    else:
+        scale = np.abs(ref).max()
+        d = np.abs(got - ref).max() / max(scale, 1e-30)
+        assert d <= tol["g_norm"], f"{name}: max|d|/max|ref| = {d:.3e}"
+
+
+def assert_parity(got, ref_loss, ref_lse, ref_zt, ref_gx, ref_gW, dtype):
+    tol = TOL[dtype]
+    rel = abs(got["loss"] - ref_loss) / max(abs(ref_loss), 1e-30)
+    assert rel <= tol["loss_rel"], f"loss {got['loss']!r} vs {ref_loss!r}: rel {rel:.3e}"
+    if ref_lse is not None:
+        d = np.abs(got["lse"] - ref_lse) / np.maximum(1.0, np.abs(ref_lse))
+        assert d.max() <= tol["lse_atol"], f"lse: max scaled |d| {d.max():.3e}"
+        np.testing.assert_allclose(got["zt"], ref_zt, rtol=tol["lse_atol"], atol=tol["lse_atol"])
+    if ref_gx is not None:
+        assert_grad_close(got["gx"], ref_gx, dtype, "grad_x")
+    if ref_gW is not None:
+        assert_grad_close(got["gW"], ref_gW, dtype, "grad_W")

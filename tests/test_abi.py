@@ -1,0 +1,110 @@
+"""C-ABI library: loads without a GPU, exports every declared symbol, and rejects
+bad arguments before any HIP call (so nothing here touches a device)."""
+import ctypes
+
+import pytest
+
+from lm_head_linear_tiled_amd import binding
+
+F32, BF16, MEAN, SUM = 0, 1, 0, 1
+OK, NULL, SHAPE, DTYPE, RED, ALIAS, ALIGN, WS, HIPERR = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = binding.header_functions()
+    assert set(names) >= {"flce_forward", "flce_backward", "flce_forward_workspace_bytes",
+                          "flce_backward_workspace_bytes", "flce_backward_min_workspace_bytes",
+                          "flce_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = binding.status_string(code)
+        assert s.startswith("FLCE_")
+    assert "unknown" in binding.status_string(99)
+
+
+def test_workspace_sizes(lib):
+    for (N, H, V) in [(64, 128, 1000), (1269, 1000, 10000), (4096, 4096, 128256), (32768, 4096, 128256)]:
+        for dt in (F32, BF16):
+            f = lib.flce_forward_workspace_bytes(N, H, V, dt)
+            b = lib.flce_backward_workspace_bytes(N, H, V, dt)
+            bmin = lib.flce_backward_min_workspace_bytes(N, H, V, dt)
+            assert f > 0 and b > 0 and 0 < bmin <= b
+    assert lib.flce_forward_workspace_bytes(0, 4, 4, F32) == 0
+    assert lib.flce_backward_workspace_bytes(4, 4, 4, 5) == 0
+    assert lib.flce_backward_min_workspace_bytes(4, -1, 4, F32) == 0
+
+
+# Fake, well-separated, 16-byte aligned addresses: every call below fails its
+# checks before a pointer is used.
+X, Wp, T, LOSS, LSE, ZT, WSP, GX, GW, GL = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(10))
+
+
+def fwd(lib, x=X, W=Wp, t=T, N=64, H=128, V=1000, dt=F32, red=MEAN, loss=LOSS, lse=LSE, zt=ZT, ws=WSP,
+        nws=None):
+    if nws is None:
+        nws = lib.flce_forward_workspace_bytes(N, H, V, dt) if N > 0 and H > 0 and V > 0 else 0
+    return lib.flce_forward(x, W, t, N, H, V, dt, red, loss, lse, zt, ws, nws, None)
+
+
+def bwd(lib, x=X, W=Wp, t=T, lse=LSE, gl=GL, N=64, H=128, V=1000, dt=F32, red=MEAN, gx=GX, gw=GW, ws=WSP,
+        nws=None):
+    if nws is None:
+        nws = lib.flce_backward_workspace_bytes(N, H, V, dt) if N > 0 and H > 0 and V > 0 else 0
+    return lib.flce_backward(x, W, t, lse, gl, N, H, V, dt, red, gx, gw, ws, nws, None)
+
+
+def test_forward_rejects(lib):
+    assert fwd(lib, x=None) == NULL
+    assert fwd(lib, t=None) == NULL
+    assert fwd(lib, loss=None) == NULL
+    assert fwd(lib, lse=None) == NULL
+    assert fwd(lib, N=0) == SHAPE
+    assert fwd(lib, V=-3) == SHAPE
+    assert fwd(lib, H=1 << 31) == SHAPE
+    assert fwd(lib, dt=2) == DTYPE
+    assert fwd(lib, red=2) == RED
+    assert fwd(lib, x=X + 8) == ALIGN
+    assert fwd(lib, W=Wp + 4) == ALIGN
+    assert fwd(lib, H=130) == ALIGN            # 130 * 4 bytes is not a multiple of 16
+    assert fwd(lib, H=132, dt=BF16) == ALIGN   # 132 * 2 bytes is not a multiple of 16
+    assert fwd(lib, lse=X + 64) == ALIAS       # lse inside x
+    assert fwd(lib, zt=LSE + 16) == ALIAS      # target_logit overlaps lse
+    assert fwd(lib, loss=WSP + 4) == ALIAS     # loss inside the workspace
+    assert fwd(lib, ws=T) == ALIAS             # workspace over the targets
+    assert fwd(lib, ws=None) == WS
+    assert fwd(lib, nws=16) == WS
+
+
+def test_backward_rejects(lib):
+    assert bwd(lib, lse=None) == NULL
+    assert bwd(lib, gl=None) == NULL
+    assert bwd(lib, gx=None) == NULL
+    assert bwd(lib, gw=None) == NULL
+    assert bwd(lib, N=-1) == SHAPE
+    assert bwd(lib, dt=9) == DTYPE
+    assert bwd(lib, red=-1) == RED
+    assert bwd(lib, x=X + 2) == ALIGN
+    assert bwd(lib, gx=Wp) == ALIAS            # grad_x over W
+    assert bwd(lib, gw=GX + 128) == ALIAS      # grad_W overlaps grad_x
+    assert bwd(lib, gx=LSE) == ALIAS           # grad_x over lse
+    assert bwd(lib, ws=GW + 64) == ALIAS       # workspace over grad_W
+    assert bwd(lib, ws=None) == WS
+    assert bwd(lib, nws=lib.flce_backward_min_workspace_bytes(64, 128, 1000, F32) - 1) == WS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        binding.flce_forward(x, torch.zeros(5, 8), torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        binding.flce_forward(x.double(), torch.zeros(5, 8).double(), torch.zeros(4, dtype=torch.int64))

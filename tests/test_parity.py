@@ -1,0 +1,173 @@
+"""HIP path against the CPU oracle, element by element, on seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lm_head_linear_tiled_amd.inputs import WORKLOADS, make_inputs, widen
+from tests.gpu_util import assert_parity, note, run_hip, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_all(x, W, t, dtype, reduction, grad_loss=1.0):
+    xf, Wf = widen(x, dtype), widen(W, dtype)
+    loss, lse, zt = oracle.forward(xf, Wf, t, reduction)
+    gx, gW = oracle.backward(xf, Wf, t, reduction, grad_loss)
+    return loss, lse, zt, gx, gW
+
+
+def check_case(gpu, N, H, V, dtype, reduction, seed=0, grad_loss=1.0, t=None, bwd_ws_bytes=None, **kw):
+    note(f"[parity] N={N} H={H} V={V} {dtype} {reduction} seed={seed} ws={bwd_ws_bytes}")
+    x, W, t0 = make_inputs(N, H, V, dtype, seed=seed, **kw)
+    t = t0 if t is None else np.asarray(t, dtype=np.int64)
+    got = run_hip(gpu, x, W, t, dtype, reduction, grad_loss, bwd_ws_bytes)
+    assert_parity(got, *oracle_all(x, W, t, dtype, reduction, grad_loss), dtype)
+    return got
+
+
+@pytest.mark.parametrize("name,reduction", [
+    ("tiny", "mean"), ("ragged", "sum"), ("ragged", "mean"), ("llama2_bf16", "mean"), ("llama2_f32", "mean"),
+])
+def test_workload_parity(gpu, name, reduction):
+    w = WORKLOADS[name]
+    check_case(gpu, w.N, w.H, w.V, w.dtype, reduction)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_multi_tile_ragged(gpu, dtype, reduction):
+    check_case(gpu, 300, 264, 1000, dtype, reduction, seed=3, grad_loss=0.7)
+
+
+@pytest.mark.parametrize("N,H,V,dtype", [
+    (1, 4, 1, "f32"), (1, 8, 2, "bf16"), (2, 8, 3, "f32"), (129, 64, 129, "bf16"), (127, 36, 257, "f32"),
+    (257, 16, 130, "bf16"),
+])
+def test_edge_shapes(gpu, N, H, V, dtype):
+    check_case(gpu, N, H, V, dtype, "sum", seed=N + V)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_targets_at_tile_edges(gpu, dtype):
+    N, H, V = 256, 128, 1000
+    t = np.array([0, V - 1, 127, 128, 255, 256, 895, 896] * (N // 8), dtype=np.int64)
+    check_case(gpu, N, H, V, dtype, "mean", seed=5, t=t)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_targets_equal(gpu, dtype):
+    """Every token has the same target: the heaviest single-row update of grad_W."""
+    N, H, V = 512, 128, 3000
+    check_case(gpu, N, H, V, dtype, "sum", seed=6, t=np.full(N, 1234))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_small_workspace_panels(gpu, dtype, reduction):
+    """The minimum workspace forces many dlogit panels and token chunks, so every
+    accumulation path (first, middle, last panel and chunk) runs."""
+    N, H, V = 700, 96, 1500
+    nmin = gpu.backward_min_workspace_bytes(N, H, V, torch.float32 if dtype == "f32" else torch.bfloat16)
+    check_case(gpu, N, H, V, dtype, reduction, seed=7, grad_loss=1.5, bwd_ws_bytes=nmin)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_w_zero_closed_form(gpu, dtype):
+    """W = 0: lse = ln V and loss = ln V (mean), grad_x = 0 exactly."""
+    N, H, V = 200, 64, 777
+    x, W, t = make_inputs(N, H, V, dtype, seed=8)
+    W = np.zeros_like(W)
+    got = run_hip(gpu, x, W, t, dtype, "mean")
+    assert abs(got["loss"] - math.log(V)) <= 2e-6 * math.log(V)
+    np.testing.assert_allclose(got["lse"], math.log(V), rtol=2e-6)
+    assert np.all(got["gx"] == 0.0)
+    xf = widen(x, dtype)
+    want = np.tile(xf.sum(axis=0) / V / N, (V, 1))
+    for i in range(N):
+        want[t[i]] -= xf[i] / N
+    tol = 1e-6 if dtype == "f32" else 1e-2 * np.abs(want).max()
+    assert np.abs(got["gW"] - want).max() <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_integer_inputs_gather_exact(gpu, dtype):
+    """Integer-valued x and W make every logit exact in fp32 whatever the
+    summation order, so the gathered target logit must equal the oracle's bit
+    for bit and lse must agree to a few fp32 ulps."""
+    N, H, V = 300, 256, 2000
+    g = np.random.Generator(np.random.PCG64(9))
+    xi = g.integers(-8, 9, size=(N, H)).astype(np.float32)
+    Wi = g.integers(-8, 9, size=(V, H)).astype(np.float32) / 64.0  # still exact in bf16 (k / 64)
+    t = g.integers(0, V, size=N)
+    if dtype == "bf16":
+        from lm_head_linear_tiled_amd.inputs import bf16_bits_from_f32
+        x, W = bf16_bits_from_f32(xi), bf16_bits_from_f32(Wi)
+    else:
+        x, W = xi, Wi
+    got = run_hip(gpu, x, W, t, dtype, "mean")
+    _, lse, zt = oracle.forward(widen(x, dtype), widen(W, dtype), t, "mean")
+    assert np.array_equal(got["zt"], zt), "target logit not bit-exact"
+    ulp = np.spacing(np.abs(lse).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got["lse"] - lse) <= 4 * ulp + 1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_extreme_logits_finite(gpu, dtype):
+    """Logits of magnitude ~1e3 stay finite and match the oracle to the rounding
+    bound of fp32 logits.  A dot product of length H accumulated in fp32 errs by at
+    most delta = (H + 2) u sum_h |x_h||W_vh| (u = 2^-24); softmax and lse inherit an
+    absolute error <= 2 delta, so each loss term errs by <= 3 delta and every
+    gradient, normalised by max|grad|, by <= 2 delta on top of the usual bar."""
+    N, H, V = 100, 64, 500
+    note(f"[parity] extreme logits {dtype}")
+    x, W, t = make_inputs(N, H, V, dtype, seed=10, w_std=40.0)
+    got = run_hip(gpu, x, W, t, dtype, "sum")
+    loss, lse, zt, gx, gW = oracle_all(x, W, t, dtype, "sum")
+    xf, Wf = widen(x, dtype), widen(W, dtype)
+    assert np.abs(xf @ Wf.T).max() > 500
+    delta = (H + 2) * 2.0 ** -24 * (np.abs(xf) @ np.abs(Wf).T).max()
+    for k in ("gx", "gW", "lse", "zt"):
+        assert np.all(np.isfinite(got[k])), k
+    assert abs(got["loss"] - loss) <= 3 * delta * N + 1e-5 * abs(loss)
+    assert np.abs(got["lse"] - lse).max() <= 2 * delta + 1e-5 * np.abs(lse).max()
+    base = 1e-4 if dtype == "f32" else 1e-2
+    for g, r in ((got["gx"], gx), (got["gW"], gW)):
+        assert np.abs(g - r).max() / np.abs(r).max() <= base + 2 * delta
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic(gpu, dtype):
+    """Forward and backward are bitwise reproducible (no atomics, fixed order)."""
+    N, H, V = 513, 128, 4099
+    x, W, t = make_inputs(N, H, V, dtype, seed=11)
+    a = run_hip(gpu, x, W, t, dtype, "mean")
+    b = run_hip(gpu, x, W, t, dtype, "mean")
+    for k in ("lse", "zt", "gx", "gW"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["loss"] == b["loss"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_loss_linear(gpu, dtype):
+    N, H, V = 130, 64, 300
+    x, W, t = make_inputs(N, H, V, dtype, seed=12)
+    a = run_hip(gpu, x, W, t, dtype, "sum", grad_loss=1.0)
+    b = run_hip(gpu, x, W, t, dtype, "sum", grad_loss=-0.25)
+    # D is formed in fp32 then rounded; a power-of-two scale commutes with every rounding
+    assert np.array_equal(b["gx"], -0.25 * a["gx"]) and np.array_equal(b["gW"], -0.25 * a["gW"])
+
+
+def test_autograd_matches_direct(gpu):
+    N, H, V = 200, 128, 999
+    x, W, t = make_inputs(N, H, V, "bf16", seed=13)
+    xd = to_dev(x, "bf16").requires_grad_(True)
+    Wd = to_dev(W, "bf16").requires_grad_(True)
+    td = torch.from_numpy(t).cuda()
+    loss = gpu.flce_loss(xd, Wd, td, "mean")
+    (2.0 * loss).backward()
+    got = run_hip(gpu, x, W, t, "bf16", "mean", grad_loss=2.0)
+    assert loss.item() == got["loss"]
+    assert np.array_equal(to_f64(xd.grad), got["gx"]) and np.array_equal(to_f64(Wd.grad), got["gW"])
