@@ -10,7 +10,7 @@
 
 namespace flce {
 
-constexpr int kTile = 128;  // square output tile of every contraction kernel
+constexpr int kTile = 256;  // square output tile of every contraction kernel
 
 struct FwdPlan {
   int tiles_tok;        // token tiles of kTile

@@ -18,7 +18,7 @@
 // gives lane i the column c0 + i for rows k0 .. k0 + 3.
 //
 // Out-of-range rows (mn >= mn_ext) and K slices (k >= k_ext) are zero-filled in
-// LDS, never read from memory.
+// LDS by the buffer unit's range check, never read from memory.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,85 +77,108 @@ __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 // Row (within the 32 x 32 block) of accumulator register r in lane l.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// LDS layout.  Tiles are stored unpadded in rows of 16-byte slots; the slot index
+// is XOR-swizzled with a function of the row so that the fragment reads below hit
+// distinct banks:
+//   K-major tile  [mn][k], 128-byte rows (BK * sizeof(T) == 128): slot ^ ((row >> 1) & 7)
+//   MN-major tile [k][mn], bfloat16 (512-byte rows):             slot ^ (4 (row & 3))
+//   MN-major tile [k][mn], float32 (1024-byte rows):             slot ^ (8 (row & 1))
+template <typename T, int MAJ>
+__device__ __forceinline__ int swz(int row) {
+  if (MAJ == K_MAJOR) return (row >> 1) & 7;
+  return sizeof(T) == 2 ? 4 * (row & 3) : 8 * (row & 1);
+}
+
 template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int NT = 256;
+  static constexpr int ES = (int)sizeof(T);
   static constexpr int VEC = ElemTraits<T>::VEC;
   static constexpr int KSTEP = ElemTraits<T>::KSTEP;
   static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
   static constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BK % KSTEP == 0 && BK % VEC == 0, "BK");
+  static_assert(BK * ES == 128, "K-major rows are 128 bytes");
 
-  static constexpr int A_ROWS = AMAJ == K_MAJOR ? BM : BK;
-  static constexpr int A_COLS = AMAJ == K_MAJOR ? BK : BM;
-  static constexpr int B_ROWS = BMAJ == K_MAJOR ? BN : BK;
-  static constexpr int B_COLS = BMAJ == K_MAJOR ? BK : BN;
-  static constexpr int A_PITCH = A_COLS + VEC;  // 16-byte pad against bank conflicts
-  static constexpr int B_PITCH = B_COLS + VEC;
-  static constexpr int A_STAGE = A_ROWS * A_PITCH;
-  static constexpr int B_STAGE = B_ROWS * B_PITCH;
-  static constexpr int LDS_ELEMS = 2 * (A_STAGE + B_STAGE);
-  static constexpr int LDS_BYTES = LDS_ELEMS * (int)sizeof(T);
-  static constexpr int A_CH = A_ROWS * A_COLS / VEC / NT;  // 16-byte chunks per thread
-  static constexpr int B_CH = B_ROWS * B_COLS / VEC / NT;
-  static_assert(A_ROWS * A_COLS % (VEC * NT) == 0 && B_ROWS * B_COLS % (VEC * NT) == 0, "chunks");
+  static constexpr int A_BYTES = BM * BK * ES;
+  static constexpr int B_BYTES = BN * BK * ES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_ELEMS = LDS_BYTES / ES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(A_BYTES % (4 * 1024) == 0 && B_BYTES % (4 * 1024) == 0, "whole 1 KiB wave loads");
 
   typedef f32x16_t Acc[FM][FN];
 
-  template <int MAJ, int COLS, int NCH>
-  static __device__ __forceinline__ void gload(const Operand<T>& op, int mn0, int k0, u32x4_t (&r)[NCH]) {
-    constexpr int CPR = COLS / VEC;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ch = (int)threadIdx.x + c * NT;
-      const int row = ch / CPR, col = (ch % CPR) * VEC;
-      const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + col;
-      const int k = MAJ == K_MAJOR ? k0 + col : k0 + row;
-      r[c] = u32x4_t{0u, 0u, 0u, 0u};
-      if (mn < op.mn_ext && k < op.k_ext) {
-        const int64_t off = MAJ == K_MAJOR ? (int64_t)mn * op.ld + k : (int64_t)k * op.ld + mn;
-        r[c] = *reinterpret_cast<const u32x4_t*>(op.ptr + off);
-      }
-    }
-  }
+  // Row length in bytes of an operand tile stored with major MAJ and mn extent MNT.
+  template <int MAJ, int MNT>
+  static constexpr int row_bytes() { return MAJ == K_MAJOR ? BK * ES : MNT * ES; }
 
-  template <int COLS, int PITCH, int NCH>
-  static __device__ __forceinline__ void lstore(T* s, const u32x4_t (&r)[NCH]) {
-    constexpr int CPR = COLS / VEC;
+  // Enqueue the global -> LDS copy of one operand tile (rows mn0.., K slice k0..).
+  // Every lane moves one 16-byte chunk per instruction straight into LDS
+  // (buffer_load ... lds: lane l of a wave instruction lands at M0 + 16 l); chunks
+  // outside the valid range get an offset past the buffer bound, which the
+  // hardware reads as zeros.  Completion is awaited by the barrier's vmcnt(0).
+  template <int MAJ, int MNT>
+  static __device__ __forceinline__ void load_tile(const Operand<T>& op, int mn0, int k0, T* lds_op) {
+    constexpr int RB = row_bytes<MAJ, MNT>();
+    constexpr int SLOTS = RB / 16;
+    constexpr int INSTR = MNT * BK * ES / 1024 / 4;  // wave instructions per wave
+    const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ch = (int)threadIdx.x + c * NT;
-      const int row = ch / CPR, col = (ch % CPR) * VEC;
-      *reinterpret_cast<u32x4_t*>(s + row * PITCH + col) = r[c];
+    for (int j = 0; j < INSTR; ++j) {
+      const int blk = j * 4 + w;  // 1 KiB block of the tile
+      const int chunk = blk * 64 + l;
+      const int row = chunk / SLOTS;
+      const int slot = (chunk % SLOTS) ^ swz<T, MAJ>(row);
+      const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
+      const int k = MAJ == K_MAJOR ? k0 + slot * VEC : k0 + row;
+      const bool ok = mn < op.mn_ext && k < op.k_ext;
+      const uint32_t off = (uint32_t)(((int64_t)row * op.ld + slot * VEC) * ES);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + blk * 1024), 16, ok ? off : 0x80000000u, 0,
+          0, 0);
     }
   }
 
   // bfloat16 operand fragment for the 32-wide block starting at mnb, k slice kk.
-  template <int MAJ, int PITCH>
+  template <int MAJ, int MNT>
   static __device__ __forceinline__ bf16x8_t frag(const bf16_t* s, int mnb, int kk) {
+    constexpr int RB = row_bytes<MAJ, MNT>();
+    const char* sb = (const char*)s;
     const int l = (int)threadIdx.x & 63;
     if (MAJ == K_MAJOR) {
-      return *reinterpret_cast<const bf16x8_t*>(s + (mnb + (l & 31)) * PITCH + kk + 8 * (l >> 5));
+      const int row = mnb + (l & 31);
+      const int slot = (kk >> 3) + (l >> 5);
+      return *reinterpret_cast<const bf16x8_t*>(sb + row * RB + 16 * (slot ^ swz<bf16_t, MAJ>(row)));
     } else {
       const int g = l >> 4, q = l & 15;
       const int col = mnb + 16 * (g & 1) + 4 * (q & 3);
       const int row = kk + 8 * (g >> 1) + (q >> 2);
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(s + row * PITCH + col));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(s + (row + 4) * PITCH + col));
+      const int cb = 16 * ((col >> 3) ^ swz<bf16_t, MAJ>(row)) + 2 * (col & 7);  // same swizzle for row + 4
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + row * RB + cb));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + (row + 4) * RB + cb));
       const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       return __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
   // float32 operand fragment (one k per lane).
-  template <int MAJ, int PITCH>
+  template <int MAJ, int MNT>
   static __device__ __forceinline__ float frag(const float* s, int mnb, int kk) {
+    constexpr int RB = row_bytes<MAJ, MNT>();
+    const char* sb = (const char*)s;
     const int l = (int)threadIdx.x & 63;
-    return MAJ == K_MAJOR ? s[(mnb + (l & 31)) * PITCH + kk + (l >> 5)]
-                          : s[(kk + (l >> 5)) * PITCH + mnb + (l & 31)];
+    if (MAJ == K_MAJOR) {
+      const int row = mnb + (l & 31), k = kk + (l >> 5);
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((k >> 2) ^ swz<float, MAJ>(row)) + 4 * (k & 3));
+    } else {
+      const int row = kk + (l >> 5), col = mnb + (l & 31);
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((col >> 2) ^ swz<float, MAJ>(row)) + 4 * (col & 3));
+    }
   }
 
   static __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -165,8 +188,41 @@ struct TileGemm {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
 
+  // LDS read instructions per fragment step, MFMAs per step, global loads per K slice.
+  static constexpr int DS_A = (AMAJ == MN_MAJOR && ES == 2) ? 2 : 1;
+  static constexpr int DS_B = (BMAJ == MN_MAJOR && ES == 2) ? 2 : 1;
+  static constexpr int N_DS = FM * DS_A + FN * DS_B;
+  static constexpr int N_MFMA = FM * FN;
+  static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / 4;
+
+  // Scheduling groups: spread NI instructions of class MASK evenly between the
+  // N_MFMA MFMAs of one step.
+  template <int NI, int MASK>
+  static __device__ __forceinline__ void interleave() {
+    constexpr int PER = NI >= N_MFMA ? NI / N_MFMA : 1;
+    constexpr int EVERY = NI >= N_MFMA ? 1 : N_MFMA / NI;
+#pragma unroll
+    for (int q = 0; q < N_MFMA; q += EVERY) {
+      __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+      __builtin_amdgcn_sched_group_barrier(MASK, PER, 0);
+    }
+  }
+
+  typedef decltype(frag<AMAJ, BM>((const T*)nullptr, 0, 0)) FragA;
+  typedef decltype(frag<BMAJ, BN>((const T*)nullptr, 0, 0)) FragB;
+
+  static __device__ __forceinline__ void load_frags(const T* as, const T* bs, int wm, int wn, int kk, FragA (&fa)[FM],
+                                                    FragB (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = frag<AMAJ, BM>(as, wm * WM + i * 32, kk);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = frag<BMAJ, BN>(bs, wn * WN + j * 32, kk);
+  }
+
   // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.  Ends with a barrier, so the caller
-  // may reuse the LDS right after.
+  // may reuse the LDS right after.  Pipelining: the direct global -> LDS copy of K
+  // slice kt+1 is in flight while slice kt is multiplied, and the LDS fragments of
+  // step s+1 are read while the MFMAs of step s run.
   static __device__ __forceinline__ void run(const Operand<T>& A, const Operand<T>& B, int m0, int n0,
                                              int K, T* lds, Acc& acc) {
     const int w = (int)threadIdx.x >> 6;
@@ -178,40 +234,38 @@ struct TileGemm {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    T* As[2] = {lds, lds + A_STAGE + B_STAGE};
-    T* Bs[2] = {lds + A_STAGE, lds + 2 * A_STAGE + B_STAGE};
-    u32x4_t ra[A_CH], rb[B_CH];
+    // Stage s: A at lds + s * STAGE, B right after it (offsets from the __shared__
+    // base keep every access on the LDS path).
+    constexpr int STAGE = STAGE_BYTES / ES;
+    constexpr int AOFF = A_BYTES / ES;
     const int KT = (K + BK - 1) / BK;
-    gload<AMAJ, A_COLS, A_CH>(A, m0, 0, ra);
-    gload<BMAJ, B_COLS, B_CH>(B, n0, 0, rb);
-    lstore<A_COLS, A_PITCH, A_CH>(As[0], ra);
-    lstore<B_COLS, B_PITCH, B_CH>(Bs[0], rb);
+    load_tile<AMAJ, BM>(A, m0, 0, lds);
+    load_tile<BMAJ, BN>(B, n0, 0, lds + AOFF);
     __syncthreads();
+    constexpr int NSTEP = BK / KSTEP;
     for (int kt = 0; kt < KT; ++kt) {
       const int cur = kt & 1;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        gload<AMAJ, A_COLS, A_CH>(A, m0, (kt + 1) * BK, ra);
-        gload<BMAJ, B_COLS, B_CH>(B, n0, (kt + 1) * BK, rb);
+      if (kt + 1 < KT) {
+        load_tile<AMAJ, BM>(A, m0, (kt + 1) * BK, lds + (cur ^ 1) * STAGE);
+        load_tile<BMAJ, BN>(B, n0, (kt + 1) * BK, lds + (cur ^ 1) * STAGE + AOFF);
       }
-      const T* as = As[cur];
-      const T* bs = Bs[cur];
+      const T* as = lds + cur * STAGE;
+      const T* bs = lds + cur * STAGE + AOFF;
+      FragA fa[2][FM];
+      FragB fb[2][FN];
+      load_frags(as, bs, wm, wn, 0, fa[0], fb[0]);
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += KSTEP) {
-        decltype(frag<AMAJ, A_PITCH>(as, 0, 0)) fa[FM];
-        decltype(frag<BMAJ, B_PITCH>(bs, 0, 0)) fb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = frag<AMAJ, A_PITCH>(as, wm * WM + i * 32, kk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = frag<BMAJ, B_PITCH>(bs, wn * WN + j * 32, kk);
+      for (int s = 0; s < NSTEP; ++s) {
+        if (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
-      }
-      if (more) {
-        lstore<A_COLS, A_PITCH, A_CH>(As[cur ^ 1], ra);
-        lstore<B_COLS, B_PITCH, B_CH>(Bs[cur ^ 1], rb);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+        // Interleave the next step's LDS reads with this step's MFMAs (and, in the
+        // first step, the global -> LDS copies of the next K slice).
+        if (s == 0) interleave<N_VMEM, 0x020>();
+        if (s + 1 < NSTEP) interleave<N_DS, 0x100>();
+        __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
     }
