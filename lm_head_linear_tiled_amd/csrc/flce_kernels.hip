@@ -28,28 +28,54 @@ namespace flce {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+#ifndef FLCE_BK_BF16
+#define FLCE_BK_BF16 64
+#endif
+#ifndef FLCE_NSTAGE_BF16
+#define FLCE_NSTAGE_BF16 2
+#endif
+#ifndef FLCE_BK_F32
+#define FLCE_BK_F32 32
+#endif
+#ifndef FLCE_NSTAGE_F32
+#define FLCE_NSTAGE_F32 2
+#endif
+#ifndef FLCE_WAVES_M
+#define FLCE_WAVES_M 4
+#endif
+#ifndef FLCE_WAVES_N
+#define FLCE_WAVES_N 2
+#endif
+
+// K slice width and LDS pipeline depth per element type: 128-byte K slices in two
+// stages (one slice in flight while one is multiplied; deeper pipelines measured
+// no faster), and the wave grid of a 256 x 256 tile.
+constexpr int kThreads = 64 * FLCE_WAVES_M * FLCE_WAVES_N;
+
 template <typename T>
 struct Cfg;
 template <>
 struct Cfg<bf16_t> {
-  static constexpr int BK = 64;
+  static constexpr int BK = FLCE_BK_BF16;
+  static constexpr int NS = FLCE_NSTAGE_BF16;
 };
 template <>
 struct Cfg<float> {
-  static constexpr int BK = 32;
+  static constexpr int BK = FLCE_BK_F32;
+  static constexpr int NS = FLCE_NSTAGE_F32;
 };
 
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void fwd_partial(const T* __restrict__ x, const T* __restrict__ W,
+__global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x, const T* __restrict__ W,
                                                    const int64_t* __restrict__ target, int N, int H, int V,
                                                    int tiles_tok, int tiles_per_split, int Np,
                                                    float* __restrict__ part_m, float* __restrict__ part_s,
                                                    float* __restrict__ zt_out) {
   // S^T tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major).
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
 
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
@@ -59,8 +85,8 @@ __global__ __launch_bounds__(256) void fwd_partial(const T* __restrict__ x, cons
   const int vt_begin = split * tiles_per_split;
   const int vt_end = min(tiles_v, vt_begin + tiles_per_split);
 
-  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int l = (int)threadIdx.x & 63;
+  const int wm = G::wave_m(), wn = G::wave_n();
 
   const Operand<T> A{W, H, V, H};
   const Operand<T> B{x, H, N, H};
@@ -129,24 +155,28 @@ __global__ __launch_bounds__(256) void fwd_partial(const T* __restrict__ x, cons
       mrun[j] = M;
     }
   }
-  // ... then the two waves that share the token columns.
-  float* sm = reinterpret_cast<float*>(lds);  // [2][WN] max, then [2][WN] sum
-  if (wm == 1 && l < 32) {
+  // ... then the WGM waves that share the token columns, in a fixed order.
+  float* sm = reinterpret_cast<float*>(lds);  // [WGM - 1][BN] max, then [WGM - 1][BN] sum
+  constexpr int SM = (G::WGM - 1) * kTile;
+  if (wm > 0 && l < 32) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      sm[wn * G::WN + j * 32 + l] = mrun[j];
-      sm[2 * G::WN + wn * G::WN + j * 32 + l] = srun[j];
+      sm[(wm - 1) * kTile + wn * G::WN + j * 32 + l] = mrun[j];
+      sm[SM + (wm - 1) * kTile + wn * G::WN + j * 32 + l] = srun[j];
     }
   }
   __syncthreads();
   if (wm == 0 && l < 32) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      const float mo = sm[wn * G::WN + j * 32 + l];
-      const float so = sm[2 * G::WN + wn * G::WN + j * 32 + l];
-      const float M = fmaxf(mrun[j], mo);
-      float S = 0.f;
-      if (M != -INFINITY) S = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - M) + so * __builtin_amdgcn_exp2f(mo - M);
+      float M = mrun[j], S = srun[j];
+      for (int q = 0; q < G::WGM - 1; ++q) {
+        const float mo = sm[q * kTile + wn * G::WN + j * 32 + l];
+        const float so = sm[SM + q * kTile + wn * G::WN + j * 32 + l];
+        const float Mn = fmaxf(M, mo);
+        if (Mn != -INFINITY) S = S * __builtin_amdgcn_exp2f(M - Mn) + so * __builtin_amdgcn_exp2f(mo - Mn);
+        M = Mn;
+      }
       const int tok = n0 + wn * G::WN + j * 32 + l;
       if (tok < N) {
         part_m[(int64_t)split * Np + tok] = M;
@@ -207,20 +237,20 @@ __global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block
 // Backward
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
+__global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
                                                    const int64_t* __restrict__ target,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ grad_loss, float red_scale, int N,
                                                    int H, int V, int i0, int v0, int tiles_m, int Vbp,
                                                    T* __restrict__ panel) {
   // S tile: rows = tokens (A = x, K-major), cols = vocabulary (B = W, K-major).
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
   const int tn = lid / tiles_m, tm = lid % tiles_m;
   const int m0 = i0 + tm * kTile, n0 = v0 + tn * kTile;
-  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int l = (int)threadIdx.x & 63;
+  const int wm = G::wave_m(), wn = G::wave_n();
 
   const Operand<T> A{x, H, N, H};
   const Operand<T> B{W, H, V, H};
@@ -252,17 +282,17 @@ __global__ __launch_bounds__(256) void bwd_dlogits(const T* __restrict__ x, cons
 // grad_W[v0 + m, h] for m in the panel: A = panel as [k = token][m = vocab]
 // (MN-major), B = x rows i0.. as [k = token][n = hidden] (MN-major).
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
+__global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
                                                   const T* __restrict__ x, int H, int V, int i0, int v0,
                                                   int Vb, int tiles_m, T* __restrict__ gw_out,
                                                   float* __restrict__ gw_acc, int accumulate, int final) {
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
   const int tn = lid / tiles_m, tm = lid % tiles_m;
   const int m0 = tm * kTile, n0 = tn * kTile;
-  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int l = (int)threadIdx.x & 63;
+  const int wm = G::wave_m(), wn = G::wave_n();
 
   const Operand<T> A{panel, Vbp, Vbp, Kc};
   const Operand<T> B{x + (int64_t)i0 * H, H, H, Kc};
@@ -294,17 +324,17 @@ __global__ __launch_bounds__(256) void bwd_grad_w(const T* __restrict__ panel, i
 // grad_x[i0 + m, h]: A = panel as [m = token][k = vocab] (K-major), B = W rows
 // v0.. as [k = vocab][n = hidden] (MN-major).
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
+__global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
                                                   const T* __restrict__ W, int H, int N, int i0, int v0,
                                                   int tiles_m, T* __restrict__ gx_out, float* __restrict__ gx_acc,
                                                   int accumulate, int final) {
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
   const int tn = lid / tiles_m, tm = lid % tiles_m;
   const int m0 = tm * kTile, n0 = tn * kTile;
-  const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int l = (int)threadIdx.x & 63;
+  const int wm = G::wave_m(), wn = G::wave_n();
 
   const Operand<T> A{panel, Vbp, Kc, Vbp};
   const Operand<T> B{W + (int64_t)v0 * H, H, H, Kv};
@@ -343,7 +373,7 @@ static hipError_t launch_fwd_t(const FwdPlan& p, const void* x, const void* W, c
                                double scale, float* loss, hipStream_t st, Recorder& rec) {
   const int grid = p.tiles_tok * p.splits;
   rec.start();
-  hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(256), 0, st, (const T*)x, (const T*)W, target, N, H, V,
+  hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(kThreads), 0, st, (const T*)x, (const T*)W, target, N, H, V,
                      p.tiles_tok, p.tiles_per_split, p.Np, part_m, part_s, zt);
   rec.after(FLCE_K_FWD_PARTIAL);
   const int nb = (N + 255) / 256;
@@ -390,18 +420,18 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int Kc = min(p.Nc, N - i0);
       const int tiles_m = (Kc + kTile - 1) / kTile;
       const int tiles_n = (Kv + kTile - 1) / kTile;
-      hipLaunchKernelGGL(bwd_dlogits<T>, dim3(tiles_m * tiles_n), dim3(256), 0, st, x, W, target, lse, grad_loss,
+      hipLaunchKernelGGL(bwd_dlogits<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
                          red_scale, N, H, V, i0, v0, tiles_m, Vbp, panel);
       rec.after(FLCE_K_BWD_DLOGITS);
       // grad_W rows of this panel accumulate over token chunks.
       const int gw_tiles_m = tiles_n;
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
-      hipLaunchKernelGGL(bwd_grad_w<T>, dim3(gw_tiles_m * tiles_h), dim3(256), 0, st, (const T*)panel, Vbp, Kc, x, H,
+      hipLaunchKernelGGL(bwd_grad_w<T>, dim3(gw_tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
                          V, i0, v0, Kv, gw_tiles_m, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
                          c == p.n_chunks - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_W);
       // grad_x rows of this chunk accumulate over vocabulary panels.
-      hipLaunchKernelGGL(bwd_grad_x<T>, dim3(tiles_m * tiles_h), dim3(256), 0, st, (const T*)panel, Vbp, Kc, Kv, W, H,
+      hipLaunchKernelGGL(bwd_grad_x<T>, dim3(tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, Kv, W, H,
                          N, i0, v0, tiles_m, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_X);
     }

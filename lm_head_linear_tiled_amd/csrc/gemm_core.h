@@ -1,6 +1,6 @@
 // Tiled MFMA contraction core for gfx950 (CDNA4, wave64).
 //
-// One workgroup of 256 threads (4 waves in a 2 x 2 grid) computes a BM x BN
+// One workgroup of WGM x WGN waves computes a BM x BN
 // float32 tile C[m][n] = sum_k A(m, k) * B(n, k) into registers, streaming K in
 // BK-wide slices through double-buffered LDS.  Each operand is stored either
 // K-major ([mn][k], k contiguous, e.g. x [N,H] and W [V,H] contracted over H) or
@@ -79,35 +79,43 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 
 // LDS layout.  Tiles are stored unpadded in rows of 16-byte slots; the slot index
 // is XOR-swizzled with a function of the row so that the fragment reads below hit
-// distinct banks:
-//   K-major tile  [mn][k], 128-byte rows (BK * sizeof(T) == 128): slot ^ ((row >> 1) & 7)
-//   MN-major tile [k][mn], bfloat16 (512-byte rows):             slot ^ (4 (row & 3))
-//   MN-major tile [k][mn], float32 (1024-byte rows):             slot ^ (8 (row & 1))
-template <typename T, int MAJ>
+// distinct banks (64 banks of 4 bytes: 256 bytes per bank cycle):
+//   K-major tile  [mn][k], RB-byte rows (RB = BK * sizeof(T), 64 or 128): the
+//       256 / RB rows that share a bank cycle differ in bank half / quarter, and
+//       slot ^ ((row / (256 / RB)) % (RB / 16)) spreads the next rows over slots;
+//   MN-major tile [k][mn], bfloat16 (512-byte rows):  slot ^ (4 (row & 3))
+//   MN-major tile [k][mn], float32 (1024-byte rows):  slot ^ (8 (row & 1))
+template <typename T, int MAJ, int RB>
 __device__ __forceinline__ int swz(int row) {
-  if (MAJ == K_MAJOR) return (row >> 1) & 7;
+  if (MAJ == K_MAJOR) return (row / (256 / RB)) % (RB / 16);
   return sizeof(T) == 2 ? 4 * (row & 3) : 8 * (row & 1);
 }
 
-template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ>
+template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ, int NSTAGE_ = 2, int WGM_ = 2, int WGN_ = 2>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
-  static constexpr int NT = 256;
+  static constexpr int NSTAGE = NSTAGE_;  // LDS stages: NSTAGE - 1 K slices in flight
+  static constexpr int WGM = WGM_, WGN = WGN_;  // wave grid over the tile
+  static constexpr int NWAVES = WGM * WGN;
+  static constexpr int NT = 64 * NWAVES;
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VEC = ElemTraits<T>::VEC;
   static constexpr int KSTEP = ElemTraits<T>::KSTEP;
-  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   static constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BK * ES == 128, "K-major rows are 128 bytes");
+  static_assert(BK * ES == 128 || BK * ES == 64, "K-major rows are 64 or 128 bytes");
 
   static constexpr int A_BYTES = BM * BK * ES;
   static constexpr int B_BYTES = BN * BK * ES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   static constexpr int LDS_ELEMS = LDS_BYTES / ES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(A_BYTES % (4 * 1024) == 0 && B_BYTES % (4 * 1024) == 0, "whole 1 KiB wave loads");
+  static_assert(A_BYTES % (NWAVES * 1024) == 0 && B_BYTES % (NWAVES * 1024) == 0, "whole 1 KiB wave loads");
+
+  static __device__ __forceinline__ int wave_m() { return ((int)threadIdx.x >> 6) / WGN; }
+  static __device__ __forceinline__ int wave_n() { return ((int)threadIdx.x >> 6) % WGN; }
 
   typedef f32x16_t Acc[FM][FN];
 
@@ -124,16 +132,16 @@ struct TileGemm {
   static __device__ __forceinline__ void load_tile(const Operand<T>& op, int mn0, int k0, T* lds_op) {
     constexpr int RB = row_bytes<MAJ, MNT>();
     constexpr int SLOTS = RB / 16;
-    constexpr int INSTR = MNT * BK * ES / 1024 / 4;  // wave instructions per wave
+    constexpr int INSTR = MNT * BK * ES / 1024 / NWAVES;  // wave instructions per wave
     const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
     const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < INSTR; ++j) {
-      const int blk = j * 4 + w;  // 1 KiB block of the tile
+      const int blk = j * NWAVES + w;  // 1 KiB block of the tile
       const int chunk = blk * 64 + l;
       const int row = chunk / SLOTS;
-      const int slot = (chunk % SLOTS) ^ swz<T, MAJ>(row);
+      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
       const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
       const int k = MAJ == K_MAJOR ? k0 + slot * VEC : k0 + row;
       const bool ok = mn < op.mn_ext && k < op.k_ext;
@@ -153,12 +161,12 @@ struct TileGemm {
     if (MAJ == K_MAJOR) {
       const int row = mnb + (l & 31);
       const int slot = (kk >> 3) + (l >> 5);
-      return *reinterpret_cast<const bf16x8_t*>(sb + row * RB + 16 * (slot ^ swz<bf16_t, MAJ>(row)));
+      return *reinterpret_cast<const bf16x8_t*>(sb + row * RB + 16 * (slot ^ swz<bf16_t, MAJ, RB>(row)));
     } else {
       const int g = l >> 4, q = l & 15;
       const int col = mnb + 16 * (g & 1) + 4 * (q & 3);
       const int row = kk + 8 * (g >> 1) + (q >> 2);
-      const int cb = 16 * ((col >> 3) ^ swz<bf16_t, MAJ>(row)) + 2 * (col & 7);  // same swizzle for row + 4
+      const int cb = 16 * ((col >> 3) ^ swz<bf16_t, MAJ, RB>(row)) + 2 * (col & 7);  // same swizzle for row + 4
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + row * RB + cb));
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + (row + 4) * RB + cb));
       const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -174,10 +182,10 @@ struct TileGemm {
     const int l = (int)threadIdx.x & 63;
     if (MAJ == K_MAJOR) {
       const int row = mnb + (l & 31), k = kk + (l >> 5);
-      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((k >> 2) ^ swz<float, MAJ>(row)) + 4 * (k & 3));
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((k >> 2) ^ swz<float, MAJ, RB>(row)) + 4 * (k & 3));
     } else {
       const int row = kk + (l >> 5), col = mnb + (l & 31);
-      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((col >> 2) ^ swz<float, MAJ>(row)) + 4 * (col & 3));
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((col >> 2) ^ swz<float, MAJ, RB>(row)) + 4 * (col & 3));
     }
   }
 
@@ -193,7 +201,7 @@ struct TileGemm {
   static constexpr int DS_B = (BMAJ == MN_MAJOR && ES == 2) ? 2 : 1;
   static constexpr int N_DS = FM * DS_A + FN * DS_B;
   static constexpr int N_MFMA = FM * FN;
-  static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / 4;
+  static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / NWAVES;
 
   // Scheduling groups: spread NI instructions of class MASK evenly between the
   // N_MFMA MFMAs of one step.
@@ -219,14 +227,22 @@ struct TileGemm {
     for (int j = 0; j < FN; ++j) fb[j] = frag<BMAJ, BN>(bs, wn * WN + j * 32, kk);
   }
 
+  // Wait until at most N of this wave's global -> LDS copies are outstanding, then
+  // meet the other waves.  The asm is also a compiler memory barrier.
+  template <int N>
+  static __device__ __forceinline__ void wait_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  }
+
   // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.  Ends with a barrier, so the caller
-  // may reuse the LDS right after.  Pipelining: the direct global -> LDS copy of K
-  // slice kt+1 is in flight while slice kt is multiplied, and the LDS fragments of
-  // step s+1 are read while the MFMAs of step s run.
+  // may reuse the LDS right after.  Pipelining: K slice kt + NSTAGE - 1 is copied
+  // global -> LDS while slice kt is multiplied (every slice issues the same number
+  // of copies, slices past K read zeros, so the wait count is a constant), and the
+  // LDS fragments of step s+1 are read while the MFMAs of step s run.
   static __device__ __forceinline__ void run(const Operand<T>& A, const Operand<T>& B, int m0, int n0,
                                              int K, T* lds, Acc& acc) {
-    const int w = (int)threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = wave_m(), wn = wave_n();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -239,16 +255,22 @@ struct TileGemm {
     constexpr int STAGE = STAGE_BYTES / ES;
     constexpr int AOFF = A_BYTES / ES;
     const int KT = (K + BK - 1) / BK;
-    load_tile<AMAJ, BM>(A, m0, 0, lds);
-    load_tile<BMAJ, BN>(B, n0, 0, lds + AOFF);
-    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st) {
+      load_tile<AMAJ, BM>(A, m0, st * BK, lds + st * STAGE);
+      load_tile<BMAJ, BN>(B, n0, st * BK, lds + st * STAGE + AOFF);
+    }
     constexpr int NSTEP = BK / KSTEP;
     for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-        load_tile<AMAJ, BM>(A, m0, (kt + 1) * BK, lds + (cur ^ 1) * STAGE);
-        load_tile<BMAJ, BN>(B, n0, (kt + 1) * BK, lds + (cur ^ 1) * STAGE + AOFF);
+      // slice kt has landed once only the NSTAGE - 2 younger slices are in flight
+      wait_and_barrier<(NSTAGE - 2) * N_VMEM>();
+      {
+        const int nk = kt + NSTAGE - 1;  // refills the stage that slice kt - 1 used
+        const int st = nk % NSTAGE;
+        load_tile<AMAJ, BM>(A, m0, nk * BK, lds + st * STAGE);
+        load_tile<BMAJ, BN>(B, n0, nk * BK, lds + st * STAGE + AOFF);
       }
+      const int cur = kt % NSTAGE;
       const T* as = lds + cur * STAGE;
       const T* bs = lds + cur * STAGE + AOFF;
       FragA fa[2][FM];
@@ -267,8 +289,9 @@ struct TileGemm {
         if (s + 1 < NSTEP) interleave<N_DS, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
     }
+    // drain the trailing (all-zero) copies before the LDS is reused
+    wait_and_barrier<0>();
   }
 };
 
