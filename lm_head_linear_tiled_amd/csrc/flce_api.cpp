@@ -18,7 +18,10 @@ using flce::FwdPlan;
 using flce::kTile;
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;     // keeps every int index in range
-constexpr int kFwdTargetWorkgroups = 2048;         // 8 per CU on a 256-CU part
+#ifndef FLCE_FWD_TARGET_WGS
+#define FLCE_FWD_TARGET_WGS 512
+#endif
+constexpr int kFwdTargetWorkgroups = FLCE_FWD_TARGET_WGS;  // forward workgroups to aim for (256 CUs)
 constexpr size_t kDefaultPanelBytes = 64u << 20;   // dlogit panel budget
 constexpr int kMinVocabPerPanel = 2048;
 

@@ -328,7 +328,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
                                                   const T* __restrict__ W, int H, int N, int i0, int v0,
                                                   int tiles_m, T* __restrict__ gx_out, float* __restrict__ gx_acc,
                                                   int accumulate, int final) {
+#ifdef FLCE_GX_GRID24
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, 2, 4> G;
+#else
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
+#endif
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
   const int tn = lid / tiles_m, tm = lid % tiles_m;

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace flce {
 
 typedef uint16_t bf16_t;  // bfloat16 storage bits
@@ -36,6 +38,17 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 enum Major { K_MAJOR = 0, MN_MAJOR = 1 };
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_<0, N>(f); }
 
 template <typename T>
 struct ElemTraits;
@@ -109,7 +122,13 @@ struct TileGemm {
   static constexpr int A_BYTES = BM * BK * ES;
   static constexpr int B_BYTES = BN * BK * ES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+#ifdef FLCE_L2_PREFETCH
+  static constexpr bool PREFETCH = true;
+#else
+  static constexpr bool PREFETCH = false;
+#endif
+  static constexpr int PF_BYTES = PREFETCH ? NWAVES * 256 : 0;  // dummy LDS for the prefetch DMA
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES + PF_BYTES;
   static constexpr int LDS_ELEMS = LDS_BYTES / ES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(A_BYTES % (NWAVES * 1024) == 0 && B_BYTES % (NWAVES * 1024) == 0, "whole 1 KiB wave loads");
@@ -128,16 +147,16 @@ struct TileGemm {
   // (buffer_load ... lds: lane l of a wave instruction lands at M0 + 16 l); chunks
   // outside the valid range get an offset past the buffer bound, which the
   // hardware reads as zeros.  Completion is awaited by the barrier's vmcnt(0).
-  template <int MAJ, int MNT>
+  template <int MAJ, int MNT, int J0 = 0, int J1 = MNT * BK * ES / 1024 / NWAVES>
   static __device__ __forceinline__ void load_tile(const Operand<T>& op, int mn0, int k0, T* lds_op) {
     constexpr int RB = row_bytes<MAJ, MNT>();
     constexpr int SLOTS = RB / 16;
-    constexpr int INSTR = MNT * BK * ES / 1024 / NWAVES;  // wave instructions per wave
+    if constexpr (J0 >= J1) return;
     const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
     const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < INSTR; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int blk = j * NWAVES + w;  // 1 KiB block of the tile
       const int chunk = blk * 64 + l;
       const int row = chunk / SLOTS;
@@ -150,6 +169,46 @@ struct TileGemm {
           rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + blk * 1024), 16, ok ? off : 0x80000000u, 0,
           0, 0);
     }
+  }
+
+  // Touch every 128-byte line of K slice k0 of both operand tiles (one 4-byte DMA
+  // per lane into a per-wave dummy LDS area), so the slice is in L2 by the time
+  // it is copied into LDS for real.
+  template <int MAJ, int MNT>
+  static __device__ __forceinline__ void prefetch_lines(const Operand<T>& op, int mn0, int k0, int line0,
+                                                        __amdgpu_buffer_rsrc_t& rsrc_out, uint32_t& off_out,
+                                                        bool& mine) {
+    constexpr int RB = row_bytes<MAJ, MNT>();
+    constexpr int LPR = RB / 128 > 0 ? RB / 128 : 1;  // lines per stored row
+    constexpr int LINES = MNT * BK * ES / 128;
+    const int lane_line = (int)threadIdx.x - line0;
+    mine = lane_line >= 0 && lane_line < LINES;
+    const int row = lane_line / LPR, cb = (lane_line % LPR) * 128;
+    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
+    rsrc_out = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
+    const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + cb / ES;
+    const int k = MAJ == K_MAJOR ? k0 : k0 + row;
+    const bool ok = mn < op.mn_ext && k < op.k_ext;
+    off_out = ok ? (uint32_t)((int64_t)row * op.ld * ES + cb) : 0x80000000u;
+  }
+
+  static __device__ __forceinline__ void prefetch(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
+                                                  T* lds) {
+    if (!PREFETCH) return;
+    constexpr int ALINES = BM * BK * ES / 128;
+    constexpr int BLINES = BN * BK * ES / 128;
+    static_assert(ALINES % 64 == 0 && ALINES + BLINES == NT, "one line per lane, whole waves per operand");
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t o;
+    bool m;
+    const int w = (int)threadIdx.x >> 6;
+    auto* dst = (__attribute__((address_space(3))) void*)((char*)lds + NSTAGE * STAGE_BYTES + w * 256);
+    // every wave issues exactly one DMA (wave-uniform instruction count)
+    if (w < ALINES / 64)
+      prefetch_lines<AMAJ, BM>(A, m0, k0, 0, r, o, m);
+    else
+      prefetch_lines<BMAJ, BN>(B, n0, k0, ALINES, r, o, m);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, m ? o : 0x80000000u, 0, 0, 0);
   }
 
   // bfloat16 operand fragment for the 32-wide block starting at mnb, k slice kk.
@@ -202,6 +261,36 @@ struct TileGemm {
   static constexpr int N_DS = FM * DS_A + FN * DS_B;
   static constexpr int N_MFMA = FM * FN;
   static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / NWAVES;
+
+  // The copies of one K slice (A's then B's wave instructions, N_VMEM in all) are
+  // spread over the first VSTEPS fragment steps, VPER per step, so that the eight
+  // waves do not flood the texture-address queue at the start of a slice.
+  static constexpr int NSTEP_ = BK / KSTEP;
+  static constexpr int VSTEPS = NSTEP_ > 1 ? NSTEP_ - 1 : 1;
+  static constexpr int VPER = (N_VMEM + VSTEPS - 1) / VSTEPS;
+  static constexpr int INSTR_A = BM * BK * ES / 1024 / NWAVES;
+
+  // Issue copy instructions [C0, C1) of the combined A-then-B sequence.
+  template <int C0, int C1>
+  static __device__ __forceinline__ void load_part(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
+                                                   T* stage) {
+    constexpr int A0 = C0 < INSTR_A ? C0 : INSTR_A, A1 = C1 < INSTR_A ? C1 : INSTR_A;
+    constexpr int B0 = (C0 > INSTR_A ? C0 : INSTR_A) - INSTR_A, B1 = (C1 > INSTR_A ? C1 : INSTR_A) - INSTR_A;
+    load_tile<AMAJ, BM, A0, A1>(A, m0, k0, stage);
+    load_tile<BMAJ, BN, B0, B1>(B, n0, k0, stage + A_BYTES / ES);
+  }
+
+  template <int S>
+  static __device__ __forceinline__ void load_step(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
+                                                   T* stage) {
+    constexpr int C0 = S * VPER < N_VMEM ? S * VPER : N_VMEM;
+    constexpr int C1 = (S + 1) * VPER < N_VMEM ? (S + 1) * VPER : N_VMEM;
+    if constexpr (S < VSTEPS) load_part<C0, C1>(A, B, m0, n0, k0, stage);
+  }
+  static constexpr int vmem_in_step(int s) {
+    return s < VSTEPS ? ((s + 1) * VPER < N_VMEM ? (s + 1) * VPER : N_VMEM) - (s * VPER < N_VMEM ? s * VPER : N_VMEM)
+                      : 0;
+  }
 
   // Scheduling groups: spread NI instructions of class MASK evenly between the
   // N_MFMA MFMAs of one step.
@@ -261,34 +350,35 @@ struct TileGemm {
       load_tile<BMAJ, BN>(B, n0, st * BK, lds + st * STAGE + AOFF);
     }
     constexpr int NSTEP = BK / KSTEP;
+    if (PREFETCH) prefetch(A, B, m0, n0, (NSTAGE - 1) * BK, lds);
     for (int kt = 0; kt < KT; ++kt) {
-      // slice kt has landed once only the NSTAGE - 2 younger slices are in flight
-      wait_and_barrier<(NSTAGE - 2) * N_VMEM>();
-      {
-        const int nk = kt + NSTAGE - 1;  // refills the stage that slice kt - 1 used
-        const int st = nk % NSTAGE;
-        load_tile<AMAJ, BM>(A, m0, nk * BK, lds + st * STAGE);
-        load_tile<BMAJ, BN>(B, n0, nk * BK, lds + st * STAGE + AOFF);
-      }
+      // slice kt has landed once only the NSTAGE - 2 younger slices (and the
+      // line prefetch issued after them) are in flight
+      wait_and_barrier<(NSTAGE - 2) * N_VMEM + (PREFETCH ? 1 : 0)>();
+      const int nk = kt + NSTAGE - 1;  // refills the stage that slice kt - 1 used
+      T* const nstage = lds + (nk % NSTAGE) * STAGE;
       const int cur = kt % NSTAGE;
       const T* as = lds + cur * STAGE;
       const T* bs = lds + cur * STAGE + AOFF;
       FragA fa[2][FM];
       FragB fb[2][FN];
       load_frags(as, bs, wm, wn, 0, fa[0], fb[0]);
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        if (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      static_for<NSTEP>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        load_step<s>(A, B, m0, n0, nk * BK, nstage);
+        if (PREFETCH && s == 0) prefetch(A, B, m0, n0, (nk + 1) * BK, lds);
+        if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-        // Interleave the next step's LDS reads with this step's MFMAs (and, in the
-        // first step, the global -> LDS copies of the next K slice).
-        if (s == 0) interleave<N_VMEM, 0x020>();
-        if (s + 1 < NSTEP) interleave<N_DS, 0x100>();
+        // Interleave this step's share of the next slice's global -> LDS copies
+        // and the next step's LDS reads with this step's MFMAs.
+        if constexpr (vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0) > 0)
+          interleave<vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0), 0x020>();
+        if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
     // drain the trailing (all-zero) copies before the LDS is reused
     wait_and_barrier<0>();
