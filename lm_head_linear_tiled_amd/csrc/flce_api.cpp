@@ -22,7 +22,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;     // keeps every int index in ra
 #define FLCE_FWD_TARGET_WGS 512
 #endif
 constexpr int kFwdTargetWorkgroups = FLCE_FWD_TARGET_WGS;  // forward workgroups to aim for (256 CUs)
-constexpr size_t kDefaultPanelBytes = 64u << 20;   // dlogit panel budget
+#ifndef FLCE_PANEL_MB
+#define FLCE_PANEL_MB 128
+#endif
+constexpr size_t kDefaultPanelBytes = size_t(FLCE_PANEL_MB) << 20;  // dlogit panel budget
 constexpr int kMinVocabPerPanel = 2048;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

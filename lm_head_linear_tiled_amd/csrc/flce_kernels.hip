@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
 
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  const int split = lid / tiles_tok, tt = lid % tiles_tok;
+  int tt, split;
+  grouped_tile(lid, tiles_tok, (int)gridDim.x / tiles_tok, tt, split);
   const int n0 = tt * kTile;
   const int tiles_v = (V + kTile - 1) / kTile;
   const int vt_begin = split * tiles_per_split;
@@ -247,7 +248,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
   const int m0 = i0 + tm * kTile, n0 = v0 + tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
@@ -286,10 +288,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
                                                   const T* __restrict__ x, int H, int V, int i0, int v0,
                                                   int Vb, int tiles_m, T* __restrict__ gw_out,
                                                   float* __restrict__ gw_acc, int accumulate, int final) {
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
@@ -328,14 +332,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
                                                   const T* __restrict__ W, int H, int N, int i0, int v0,
                                                   int tiles_m, T* __restrict__ gx_out, float* __restrict__ gx_acc,
                                                   int accumulate, int final) {
-#ifdef FLCE_GX_GRID24
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, 2, 4> G;
-#else
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
-#endif
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  const int tn = lid / tiles_m, tm = lid % tiles_m;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();

@@ -104,7 +104,14 @@ __device__ __forceinline__ int swz(int row) {
   return sizeof(T) == 2 ? 4 * (row & 3) : 8 * (row & 1);
 }
 
-template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ, int NSTAGE_ = 2, int WGM_ = 2, int WGN_ = 2>
+// How a K slice travels from global memory to LDS.
+enum Staging {
+  STAGE_DMA = 0,  // buffer_load ... lds: straight into LDS, no registers
+  STAGE_REG = 1   // 16-byte buffer loads into registers, then ds_write_b128
+};
+
+template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ, int NSTAGE_ = 2, int WGM_ = 2, int WGN_ = 2,
+          int STAGING = STAGE_DMA>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int NSTAGE = NSTAGE_;  // LDS stages: NSTAGE - 1 K slices in flight
@@ -270,6 +277,37 @@ struct TileGemm {
   static constexpr int VPER = (N_VMEM + VSTEPS - 1) / VSTEPS;
   static constexpr int INSTR_A = BM * BK * ES / 1024 / NWAVES;
 
+  // Register-staged copies: buffer loads (out-of-range lanes read zeros) into
+  // registers, written to the same swizzled LDS slots later.
+  template <int MAJ, int MNT, int J0, int J1>
+  static __device__ __forceinline__ void rload(const Operand<T>& op, int mn0, int k0, u32x4_t* r) {
+    constexpr int RB = row_bytes<MAJ, MNT>();
+    constexpr int SLOTS = RB / 16;
+    if constexpr (J0 >= J1) return;
+    const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
+#pragma unroll
+    for (int j = J0; j < J1; ++j) {
+      const int blk = j * NWAVES + w;
+      const int chunk = blk * 64 + l;
+      const int row = chunk / SLOTS;
+      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
+      const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
+      const int k = MAJ == K_MAJOR ? k0 + slot * VEC : k0 + row;
+      const bool ok = mn < op.mn_ext && k < op.k_ext;
+      const uint32_t off = (uint32_t)(((int64_t)row * op.ld + slot * VEC) * ES);
+      r[j - J0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? off : 0x80000000u, 0, 0));
+    }
+  }
+  template <int MNT, int J0, int J1>
+  static __device__ __forceinline__ void rstore(T* lds_op, const u32x4_t* r) {
+    const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+#pragma unroll
+    for (int j = J0; j < J1; ++j)
+      *reinterpret_cast<u32x4_t*>((char*)lds_op + (j * NWAVES + w) * 1024 + 16 * l) = r[j - J0];
+  }
+
   // Issue copy instructions [C0, C1) of the combined A-then-B sequence.
   template <int C0, int C1>
   static __device__ __forceinline__ void load_part(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
@@ -321,7 +359,10 @@ struct TileGemm {
   template <int N>
   static __device__ __forceinline__ void wait_and_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    if constexpr (STAGING == STAGE_REG)  // the staged ds_writes must also have landed
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
   }
 
   // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.  Ends with a barrier, so the caller
@@ -363,9 +404,23 @@ struct TileGemm {
       FragA fa[2][FM];
       FragB fb[2][FN];
       load_frags(as, bs, wm, wn, 0, fa[0], fb[0]);
+      u32x4_t rg[STAGING == STAGE_REG ? N_VMEM : 1];
       static_for<NSTEP>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
-        load_step<s>(A, B, m0, n0, nk * BK, nstage);
+        if constexpr (STAGING == STAGE_REG) {
+          // loads at the first step, LDS writes at the last: a whole slice of
+          // MFMAs covers the load latency
+          if constexpr (s == 0) {
+            rload<AMAJ, BM, 0, INSTR_A>(A, m0, nk * BK, rg);
+            rload<BMAJ, BN, 0, N_VMEM - INSTR_A>(B, n0, nk * BK, rg + INSTR_A);
+          }
+          if constexpr (s == NSTEP - 1) {
+            rstore<BM, 0, INSTR_A>(nstage, rg);
+            rstore<BN, 0, N_VMEM - INSTR_A>(nstage + A_BYTES / ES, rg + INSTR_A);
+          }
+        } else {
+          load_step<s>(A, B, m0, n0, nk * BK, nstage);
+        }
         if (PREFETCH && s == 0) prefetch(A, B, m0, n0, (nk + 1) * BK, lds);
         if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
@@ -374,8 +429,11 @@ struct TileGemm {
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
         // Interleave this step's share of the next slice's global -> LDS copies
         // and the next step's LDS reads with this step's MFMAs.
-        if constexpr (vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0) > 0)
+        if constexpr (STAGING == STAGE_REG) {
+          if constexpr (s == 0) interleave<N_VMEM, 0x020>();
+        } else if constexpr (vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0) > 0) {
           interleave<vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0), 0x020>();
+        }
         if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -391,6 +449,30 @@ __device__ __forceinline__ int xcd_grouped_id(int b, int G) {
   const int q = G >> 3, r = G & 7;
   const int x = b & 7;
   return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+#ifndef FLCE_GROUP_M
+#define FLCE_GROUP_M 4
+#endif
+
+// Tile (tm, tn) of a tiles_m x tiles_n grid for logical id t, walking groups of
+// GM tile rows column by column: any GM * c consecutive ids form a GM x c block,
+// so the 32 workgroups an XCD runs at once share GM row tiles and 32 / GM column
+// tiles of the operands in its L2 (GM = 1: plain row-fastest order).
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = FLCE_GROUP_M;
+  if (GM <= 1) {
+    tm = t % tiles_m;
+    tn = t / tiles_m;
+    return;
+  }
+  const int per_group = GM * tiles_n;
+  const int g = t / per_group;
+  const int first = g * GM;
+  const int rows = min(GM, tiles_m - first);
+  const int in = t - g * per_group;
+  tm = first + in % rows;
+  tn = in / rows;
 }
 
 }  // namespace flce
