@@ -129,13 +129,7 @@ struct TileGemm {
   static constexpr int A_BYTES = BM * BK * ES;
   static constexpr int B_BYTES = BN * BK * ES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-#ifdef FLCE_L2_PREFETCH
-  static constexpr bool PREFETCH = true;
-#else
-  static constexpr bool PREFETCH = false;
-#endif
-  static constexpr int PF_BYTES = PREFETCH ? NWAVES * 256 : 0;  // dummy LDS for the prefetch DMA
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES + PF_BYTES;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   static constexpr int LDS_ELEMS = LDS_BYTES / ES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(A_BYTES % (NWAVES * 1024) == 0 && B_BYTES % (NWAVES * 1024) == 0, "whole 1 KiB wave loads");
@@ -176,46 +170,6 @@ struct TileGemm {
           rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + blk * 1024), 16, ok ? off : 0x80000000u, 0,
           0, 0);
     }
-  }
-
-  // Touch every 128-byte line of K slice k0 of both operand tiles (one 4-byte DMA
-  // per lane into a per-wave dummy LDS area), so the slice is in L2 by the time
-  // it is copied into LDS for real.
-  template <int MAJ, int MNT>
-  static __device__ __forceinline__ void prefetch_lines(const Operand<T>& op, int mn0, int k0, int line0,
-                                                        __amdgpu_buffer_rsrc_t& rsrc_out, uint32_t& off_out,
-                                                        bool& mine) {
-    constexpr int RB = row_bytes<MAJ, MNT>();
-    constexpr int LPR = RB / 128 > 0 ? RB / 128 : 1;  // lines per stored row
-    constexpr int LINES = MNT * BK * ES / 128;
-    const int lane_line = (int)threadIdx.x - line0;
-    mine = lane_line >= 0 && lane_line < LINES;
-    const int row = lane_line / LPR, cb = (lane_line % LPR) * 128;
-    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
-    rsrc_out = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
-    const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + cb / ES;
-    const int k = MAJ == K_MAJOR ? k0 : k0 + row;
-    const bool ok = mn < op.mn_ext && k < op.k_ext;
-    off_out = ok ? (uint32_t)((int64_t)row * op.ld * ES + cb) : 0x80000000u;
-  }
-
-  static __device__ __forceinline__ void prefetch(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
-                                                  T* lds) {
-    if (!PREFETCH) return;
-    constexpr int ALINES = BM * BK * ES / 128;
-    constexpr int BLINES = BN * BK * ES / 128;
-    static_assert(ALINES % 64 == 0 && ALINES + BLINES == NT, "one line per lane, whole waves per operand");
-    __amdgpu_buffer_rsrc_t r;
-    uint32_t o;
-    bool m;
-    const int w = (int)threadIdx.x >> 6;
-    auto* dst = (__attribute__((address_space(3))) void*)((char*)lds + NSTAGE * STAGE_BYTES + w * 256);
-    // every wave issues exactly one DMA (wave-uniform instruction count)
-    if (w < ALINES / 64)
-      prefetch_lines<AMAJ, BM>(A, m0, k0, 0, r, o, m);
-    else
-      prefetch_lines<BMAJ, BN>(B, n0, k0, ALINES, r, o, m);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, m ? o : 0x80000000u, 0, 0, 0);
   }
 
   // bfloat16 operand fragment for the 32-wide block starting at mnb, k slice kk.
@@ -391,11 +345,9 @@ struct TileGemm {
       load_tile<BMAJ, BN>(B, n0, st * BK, lds + st * STAGE + AOFF);
     }
     constexpr int NSTEP = BK / KSTEP;
-    if (PREFETCH) prefetch(A, B, m0, n0, (NSTAGE - 1) * BK, lds);
     for (int kt = 0; kt < KT; ++kt) {
-      // slice kt has landed once only the NSTAGE - 2 younger slices (and the
-      // line prefetch issued after them) are in flight
-      wait_and_barrier<(NSTAGE - 2) * N_VMEM + (PREFETCH ? 1 : 0)>();
+      // slice kt has landed once only the NSTAGE - 2 younger slices are in flight
+      wait_and_barrier<(NSTAGE - 2) * N_VMEM>();
       const int nk = kt + NSTAGE - 1;  // refills the stage that slice kt - 1 used
       T* const nstage = lds + (nk % NSTAGE) * STAGE;
       const int cur = kt % NSTAGE;
@@ -421,7 +373,6 @@ struct TileGemm {
         } else {
           load_step<s>(A, B, m0, n0, nk * BK, nstage);
         }
-        if (PREFETCH && s == 0) prefetch(A, B, m0, n0, (nk + 1) * BK, lds);
         if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -431,8 +382,8 @@ struct TileGemm {
         // and the next step's LDS reads with this step's MFMAs.
         if constexpr (STAGING == STAGE_REG) {
           if constexpr (s == 0) interleave<N_VMEM, 0x020>();
-        } else if constexpr (vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0) > 0) {
-          interleave<vmem_in_step(s) + (PREFETCH && s == 0 ? 1 : 0), 0x020>();
+        } else if constexpr (vmem_in_step(s) > 0) {
+          interleave<vmem_in_step(s), 0x020>();
         }
         if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
