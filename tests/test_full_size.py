@@ -1,0 +1,75 @@
+"""Parity at the full benchmark sizes, in the launch configuration bench.py times
+(default workspaces), on outputs the float64 oracle can compute one by one:
+
+* lse and the target logit of sampled tokens, and their grad_x rows (each needs
+  only that token's logits);
+* grad_W rows of sampled vocabulary entries (always including targets) wherever
+  the oracle's own lse for every token is affordable (<= ~9e12 flop);
+* the loss against the oracle's full forward where that is affordable, and
+  otherwise the property loss = reduce(lse - target logit) with the sampled
+  terms matching the oracle;
+* at every size, the property sum_v grad_W[v, :] = 0 (every dlogit row sums to 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lm_head_linear_tiled_amd.inputs import WORKLOADS, make_inputs, widen
+from tests.gpu_util import TOL, note, to_dev, to_f64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+FULL_ORACLE_FLOP = 9e12  # full float64 forward on the host: ~10 s at ~1 TFLOP/s
+
+
+@pytest.mark.parametrize("name", ["llama3_4k", "llama2_4k", "llama2_32k", "llama3_8k", "llama3_16k",
+                                  "llama3_32k"])
+def test_full_size(gpu, name):
+    w = WORKLOADS[name]
+    N, H, V, dt = w.N, w.H, w.V, w.dtype
+    note(f"[full] {name} N={N} H={H} V={V} {dt}")
+    x, W, t = make_inputs(N, H, V, dt, seed=0)
+    xd, Wd, td = to_dev(x, dt), to_dev(W, dt), torch.from_numpy(t).cuda()
+    loss, lse, zt = gpu.flce_forward(xd, Wd, td, "mean", with_target_logit=True)
+    gx, gW = gpu.flce_backward(xd, Wd, td, lse, torch.ones(1, device="cuda"), "mean")
+    torch.cuda.synchronize()
+    note(f"[full] {name} GPU done")
+    tol = TOL[dt]
+
+    # property at any size: every dlogit row sums to zero, so do grad_W's columns.
+    # What remains is rounding: D is rounded to bf16 (|dD| <= 2^-9 |D|, and a dlogit
+    # row has sum_v |D_iv| <= 2 s), then grad_W is rounded to bf16, so per column h
+    # |sum_v grad_W[v,h]| <= 2^-8 s sum_i |x_ih| + 2^-9 sum_v |grad_W[v,h]| (+ fp32 sums).
+    assert torch.isfinite(gx).all() and torch.isfinite(gW).all()
+    colsum = gW.double().sum(dim=0).abs()
+    xf_abs = torch.from_numpy(np.abs(widen(x, dt)).sum(axis=0)).cuda()
+    bound = 2.0 ** -8 / N * xf_abs + 2.0 ** -9 * gW.double().abs().sum(dim=0)
+    assert bool((colsum <= 1.5 * bound + 1e-12).all()), f"sum_v grad_W exceeds its rounding bound"
+
+    g = np.random.Generator(np.random.PCG64(1))
+    rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 30, replace=False)]))
+    xf, Wf = widen(x, dt), widen(W, dt)
+    lse_h, zt_h = to_f64(lse), to_f64(zt)
+    r_lse, r_zt = oracle.forward_rows(xf, Wf, t, rows)
+    np.testing.assert_allclose(lse_h[rows], r_lse, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(r_lse).max()))
+    np.testing.assert_allclose(zt_h[rows], r_zt, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(r_zt).max()))
+
+    # grad_x rows: normalised by the largest |grad_x| of the sampled rows
+    r_gx = oracle.grad_x_rows(xf, Wf, t, rows, "mean")
+    d = np.abs(to_f64(gx[torch.from_numpy(rows).cuda()]) - r_gx).max() / np.abs(r_gx).max()
+    assert d <= (tol["g_norm"] if dt == "bf16" else 1e-4), f"grad_x rows: {d:.3e}"
+
+    # loss: consistency with the per-token terms everywhere ...
+    per = lse_h - zt_h
+    assert abs(loss.item() - per.mean()) <= 1e-6 * abs(per.mean())
+    if 2.0 * N * H * V <= FULL_ORACLE_FLOP:
+        # ... and the oracle's own full forward where affordable
+        ref_loss, ref_lse, _ = oracle.forward(xf, Wf, t, "mean")
+        note(f"[full] {name} oracle forward done")
+        assert abs(loss.item() - ref_loss) <= tol["loss_rel"] * abs(ref_loss)
+        vrows = np.unique(np.concatenate([[0, V - 1], t[rows[:8]], g.choice(V, 24, replace=False)]))
+        r_gW = oracle.grad_w_rows(xf, Wf, t, vrows, ref_lse, "mean")
+        got = to_f64(gW[torch.from_numpy(vrows).cuda()])
+        d = np.abs(got - r_gW).max() / np.abs(r_gW).max()
+        assert d <= (tol["g_norm"] if dt == "bf16" else 1e-4), f"grad_W rows: {d:.3e}"
