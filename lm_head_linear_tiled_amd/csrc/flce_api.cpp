@@ -19,7 +19,7 @@ using flce::kTile;
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;     // keeps every int index in range
 #ifndef FLCE_FWD_TARGET_WGS
-#define FLCE_FWD_TARGET_WGS 512
+#define FLCE_FWD_TARGET_WGS 256
 #endif
 constexpr int kFwdTargetWorkgroups = FLCE_FWD_TARGET_WGS;  // forward workgroups to aim for (256 CUs)
 #ifndef FLCE_PANEL_MB
@@ -146,6 +146,18 @@ flce_status check_common(const void* x, const void* W, const int64_t* target, in
 
 }  // namespace
 
+int flce::device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 extern "C" {
 
 const char* flce_status_string(flce_status s) {
@@ -233,6 +245,7 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   if (any_alias(in, 5, out, 2, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
   BwdPlan p;
   if (!ws || !plan_backward(N, H, V, dt, ws_bytes, &p)) return FLCE_ERR_WORKSPACE;
+  p.max_workgroups = flce::device_cu_count();
 
   char* base = (char*)ws;
   const float red_scale = reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f;

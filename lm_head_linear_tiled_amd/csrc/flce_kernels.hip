@@ -103,9 +103,12 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
   }
 
   typename G::Acc acc;
-  for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int m0 = vt * kTile;
-    G::run(A, B, m0, n0, H, lds, acc);
+  auto next = [&](int j, int& m0, int& tn0) {
+    m0 = (vt_begin + j) * kTile;
+    tn0 = n0;
+    return vt_begin + j < vt_end;
+  };
+  auto fold = [&](typename G::Acc& a, int m0, int) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       float tmax = -INFINITY;
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-          const float val = v < V ? acc[i][j][r] * kLog2e : -INFINITY;
+          const float val = v < V ? a[i][j][r] * kLog2e : -INFINITY;
           tmax = fmaxf(tmax, val);
         }
       const float mnew = fmaxf(mrun[j], tmax);
@@ -125,25 +128,30 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-            ssum += v < V ? __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - mnew) : 0.f;
+            ssum += v < V ? __builtin_amdgcn_exp2f(a[i][j][r] * kLog2e - mnew) : 0.f;
           }
         srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - mnew) + ssum;
         mrun[j] = mnew;
       }
-      // Target logit: exactly one lane of one workgroup holds (t, tok).
+      // Target logit: exactly one lane of one workgroup holds (t, tok); most
+      // waves hold none in a given tile and skip the search.
+      const int local0 = tgt[j] - (m0 + wm * G::WM);
+      if (__any(local0 >= 0 && local0 < G::WM)) {
 #pragma unroll
-      for (int i = 0; i < G::FM; ++i) {
-        const int local = tgt[j] - (m0 + wm * G::WM + i * 32);
-        if (local >= 0 && local < 32 && ((local >> 2) & 1) == (l >> 5)) {
-          const int rr = (local >> 3) * 4 + (local & 3);
-          float z = 0.f;
+        for (int i = 0; i < G::FM; ++i) {
+          const int local = local0 - i * 32;
+          if (local >= 0 && local < 32 && ((local >> 2) & 1) == (l >> 5)) {
+            const int rr = (local >> 3) * 4 + (local & 3);
+            float z = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z = r == rr ? acc[i][j][r] : z;
-          zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = z;
+            for (int r = 0; r < 16; ++r) z = r == rr ? a[i][j][r] : z;
+            zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = z;
+          }
         }
       }
     }
-  }
+  };
+  G::run_tiles(A, B, H, lds, acc, next, fold);
 
   // Merge the two lane halves (same token, different vocabulary rows) ...
 #pragma unroll
@@ -237,137 +245,158 @@ __global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
+// The backward kernels are persistent: one workgroup per CU walks the tiles
+// t = lid, lid + G, ... of its launch (lid: XCD-grouped id, G: grid size), each
+// tile (tm, tn) taken in the grouped order, so the copy of a tile's first K slice
+// overlaps the previous tile's last slice and epilogue.
+__device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int G = (int)gridDim.x;
+  const int t = xcd_grouped_id((int)blockIdx.x, G) + j * G;
+  if (t >= tiles_m * tiles_n) return false;
+  grouped_tile(t, tiles_m, tiles_n, tm, tn);
+  return true;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
-                                                   const int64_t* __restrict__ target,
-                                                   const float* __restrict__ lse,
-                                                   const float* __restrict__ grad_loss, float red_scale, int N,
-                                                   int H, int V, int i0, int v0, int tiles_m, int Vbp,
-                                                   T* __restrict__ panel) {
+                                                        const int64_t* __restrict__ target,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ grad_loss, float red_scale, int N,
+                                                        int H, int V, int i0, int v0, int tiles_m, int tiles_n,
+                                                        int Vbp, T* __restrict__ panel) {
   // S tile: rows = tokens (A = x, K-major), cols = vocabulary (B = W, K-major).
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  int tm, tn;
-  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
-  const int m0 = i0 + tm * kTile, n0 = v0 + tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-
   const Operand<T> A{x, H, N, H};
   const Operand<T> B{W, H, V, H};
-  typename G::Acc acc;
-  G::run(A, B, m0, n0, H, lds, acc);
-
   const float s = grad_loss[0] * red_scale;
+  auto next = [&](int j, int& m0, int& n0) {
+    int tm, tn;
+    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
+    m0 = i0 + tm * kTile;
+    n0 = v0 + tn * kTile;
+    return true;
+  };
+  auto store = [&](typename G::Acc& acc, int m0, int n0) {
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+    for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-      const bool rv = row < N;
-      const float lr = rv ? lse[row] * kLog2e : 0.f;
-      const int64_t tr = rv ? target[row] : -1;
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+        const bool rv = row < N;
+        const float lr = rv ? lse[row] * kLog2e : 0.f;
+        const int64_t tr = rv ? target[row] : -1;
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int col = n0 + wn * G::WN + j * 32 + (l & 31);
-        float d = 0.f;
-        if (rv && col < V) {
-          const float p = __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - lr);
-          d = s * (p - (col == tr ? 1.f : 0.f));
+        for (int j = 0; j < G::FN; ++j) {
+          const int col = n0 + wn * G::WN + j * 32 + (l & 31);
+          float d = 0.f;
+          if (rv && col < V) {
+            const float p = __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - lr);
+            d = s * (p - (col == tr ? 1.f : 0.f));
+          }
+          panel[(int64_t)(row - i0) * Vbp + (col - v0)] = from_f32<T>(d);
         }
-        panel[(int64_t)(row - i0) * Vbp + (col - v0)] = from_f32<T>(d);
       }
-    }
+  };
+  typename G::Acc acc;
+  G::run_tiles(A, B, H, lds, acc, next, store);
 }
 
 // grad_W[v0 + m, h] for m in the panel: A = panel as [k = token][m = vocab]
 // (MN-major), B = x rows i0.. as [k = token][n = hidden] (MN-major).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
-                                                  const T* __restrict__ x, int H, int V, int i0, int v0,
-                                                  int Vb, int tiles_m, T* __restrict__ gw_out,
-                                                  float* __restrict__ gw_acc, int accumulate, int final) {
+                                                       const T* __restrict__ x, int H, int V, int i0, int v0,
+                                                       int Vb, int tiles_m, int tiles_n, T* __restrict__ gw_out,
+                                                       float* __restrict__ gw_acc, int accumulate, int final) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  int tm, tn;
-  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
-  const int m0 = tm * kTile, n0 = tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-
   const Operand<T> A{panel, Vbp, Vbp, Kc};
   const Operand<T> B{x + (int64_t)i0 * H, H, H, Kc};
-  typename G::Acc acc;
-  G::run(A, B, m0, n0, Kc, lds, acc);
-
+  auto next = [&](int j, int& m0, int& n0) {
+    int tm, tn;
+    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
+    m0 = tm * kTile;
+    n0 = tn * kTile;
+    return true;
+  };
   // gw_out and gw_acc point at row v0 of their buffers; rows are panel-local.
+  auto store = [&](typename G::Acc& acc, int m0, int n0) {
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+    for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-      if (m >= Vb || v0 + m >= V) continue;
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+        if (m >= Vb || v0 + m >= V) continue;
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int h = n0 + wn * G::WN + j * 32 + (l & 31);
-        if (h >= H) continue;
-        const int64_t o = (int64_t)m * H + h;
-        float val = acc[i][j][r];
-        if (accumulate) val += gw_acc[o];
-        if (final)
-          gw_out[o] = from_f32<T>(val);
-        else
-          gw_acc[o] = val;
+        for (int j = 0; j < G::FN; ++j) {
+          const int h = n0 + wn * G::WN + j * 32 + (l & 31);
+          if (h >= H) continue;
+          const int64_t o = (int64_t)m * H + h;
+          float val = acc[i][j][r];
+          if (accumulate) val += gw_acc[o];
+          if (final)
+            gw_out[o] = from_f32<T>(val);
+          else
+            gw_acc[o] = val;
+        }
       }
-    }
+  };
+  typename G::Acc acc;
+  G::run_tiles(A, B, Kc, lds, acc, next, store);
 }
 
 // grad_x[i0 + m, h]: A = panel as [m = token][k = vocab] (K-major), B = W rows
 // v0.. as [k = vocab][n = hidden] (MN-major).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
-                                                  const T* __restrict__ W, int H, int N, int i0, int v0,
-                                                  int tiles_m, T* __restrict__ gx_out, float* __restrict__ gx_acc,
-                                                  int accumulate, int final) {
+                                                       const T* __restrict__ W, int H, int N, int i0, int v0,
+                                                       int tiles_m, int tiles_n, T* __restrict__ gx_out,
+                                                       float* __restrict__ gx_acc, int accumulate, int final) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
-  int tm, tn;
-  grouped_tile(lid, tiles_m, (int)gridDim.x / tiles_m, tm, tn);
-  const int m0 = tm * kTile, n0 = tn * kTile;
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-
   const Operand<T> A{panel, Vbp, Kc, Vbp};
   const Operand<T> B{W + (int64_t)v0 * H, H, H, Kv};
-  typename G::Acc acc;
-  G::run(A, B, m0, n0, Kv, lds, acc);
-
+  auto next = [&](int j, int& m0, int& n0) {
+    int tm, tn;
+    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
+    m0 = tm * kTile;
+    n0 = tn * kTile;
+    return true;
+  };
+  auto store = [&](typename G::Acc& acc, int m0, int n0) {
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+    for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-      if (m >= Kc) continue;
-      const int row = i0 + m;
-      if (row >= N) continue;
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+        if (m >= Kc) continue;
+        const int row = i0 + m;
+        if (row >= N) continue;
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int h = n0 + wn * G::WN + j * 32 + (l & 31);
-        if (h >= H) continue;
-        const int64_t o = (int64_t)row * H + h;
-        float val = acc[i][j][r];
-        if (accumulate) val += gx_acc[o];
-        if (final)
-          gx_out[o] = from_f32<T>(val);
-        else
-          gx_acc[o] = val;
+        for (int j = 0; j < G::FN; ++j) {
+          const int h = n0 + wn * G::WN + j * 32 + (l & 31);
+          if (h >= H) continue;
+          const int64_t o = (int64_t)row * H + h;
+          float val = acc[i][j][r];
+          if (accumulate) val += gx_acc[o];
+          if (final)
+            gx_out[o] = from_f32<T>(val);
+          else
+            gx_acc[o] = val;
+        }
       }
-    }
+  };
+  typename G::Acc acc;
+  G::run_tiles(A, B, Kv, lds, acc, next, store);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,19 +455,19 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int Kc = min(p.Nc, N - i0);
       const int tiles_m = (Kc + kTile - 1) / kTile;
       const int tiles_n = (Kv + kTile - 1) / kTile;
-      hipLaunchKernelGGL(bwd_dlogits<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
-                         red_scale, N, H, V, i0, v0, tiles_m, Vbp, panel);
+      auto grid = [&](int tiles) { return dim3(min(tiles, p.max_workgroups)); };
+      hipLaunchKernelGGL(bwd_dlogits<T>, grid(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
+                         red_scale, N, H, V, i0, v0, tiles_m, tiles_n, Vbp, panel);
       rec.after(FLCE_K_BWD_DLOGITS);
       // grad_W rows of this panel accumulate over token chunks.
-      const int gw_tiles_m = tiles_n;
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
-      hipLaunchKernelGGL(bwd_grad_w<T>, dim3(gw_tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
-                         V, i0, v0, Kv, gw_tiles_m, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
+      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
+                         V, i0, v0, Kv, tiles_n, tiles_h, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
                          c == p.n_chunks - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_W);
       // grad_x rows of this chunk accumulate over vocabulary panels.
-      hipLaunchKernelGGL(bwd_grad_x<T>, dim3(tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, Kv, W, H,
-                         N, i0, v0, tiles_m, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
+      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, Kv, W,
+                         H, N, i0, v0, tiles_m, tiles_h, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_X);
     }
   }

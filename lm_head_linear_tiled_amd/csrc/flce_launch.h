@@ -26,7 +26,11 @@ struct BwdPlan {
   int Ncp;                  // Nc padded to kTile
   size_t off_panel, off_gx, off_gw, total;  // workspace carving (bytes); 0-sized parts unused
   size_t gx_bytes, gw_bytes;
+  int max_workgroups;                       // persistent grid size: one workgroup per CU
 };
+
+// Compute units of the current HIP device (cached per device; 256 if the query fails).
+int device_cu_count();
 
 // Records the caller's timing events between kernel launches (no-op without one).
 struct Recorder {

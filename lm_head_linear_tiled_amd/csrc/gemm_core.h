@@ -319,78 +319,117 @@ struct TileGemm {
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
   }
 
-  // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.  Ends with a barrier, so the caller
-  // may reuse the LDS right after.  Pipelining: K slice kt + NSTAGE - 1 is copied
-  // global -> LDS while slice kt is multiplied (every slice issues the same number
-  // of copies, slices past K read zeros, so the wait count is a constant), and the
-  // LDS fragments of step s+1 are read while the MFMAs of step s run.
-  static __device__ __forceinline__ void run(const Operand<T>& A, const Operand<T>& B, int m0, int n0,
-                                             int K, T* lds, Acc& acc) {
-    const int wm = wave_m(), wn = wave_n();
+  static __device__ __forceinline__ void zero(Acc& acc) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
 
-    // Stage s: A at lds + s * STAGE, B right after it (offsets from the __shared__
-    // base keep every access on the LDS path).
+  // Multiply one K slice held in LDS stage `cur` into acc while the copy of the
+  // next slice (origin pm0/pn0, K offset pk0) goes into the other stage: the
+  // copies are spread over the first fragment steps (DMA) or loaded at the first
+  // step and written at the last (register staging), and the LDS fragment reads of
+  // step s+1 are interleaved with the MFMAs of step s.
+  static __device__ __forceinline__ void slice(const Operand<T>& A, const Operand<T>& B, T* lds, int cur, int pm0,
+                                               int pn0, int pk0, Acc& acc) {
     constexpr int STAGE = STAGE_BYTES / ES;
     constexpr int AOFF = A_BYTES / ES;
-    const int KT = (K + BK - 1) / BK;
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st) {
-      load_tile<AMAJ, BM>(A, m0, st * BK, lds + st * STAGE);
-      load_tile<BMAJ, BN>(B, n0, st * BK, lds + st * STAGE + AOFF);
-    }
     constexpr int NSTEP = BK / KSTEP;
-    for (int kt = 0; kt < KT; ++kt) {
-      // slice kt has landed once only the NSTAGE - 2 younger slices are in flight
-      wait_and_barrier<(NSTAGE - 2) * N_VMEM>();
-      const int nk = kt + NSTAGE - 1;  // refills the stage that slice kt - 1 used
-      T* const nstage = lds + (nk % NSTAGE) * STAGE;
-      const int cur = kt % NSTAGE;
-      const T* as = lds + cur * STAGE;
-      const T* bs = lds + cur * STAGE + AOFF;
-      FragA fa[2][FM];
-      FragB fb[2][FN];
-      load_frags(as, bs, wm, wn, 0, fa[0], fb[0]);
-      u32x4_t rg[STAGING == STAGE_REG ? N_VMEM : 1];
-      static_for<NSTEP>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        if constexpr (STAGING == STAGE_REG) {
-          // loads at the first step, LDS writes at the last: a whole slice of
-          // MFMAs covers the load latency
-          if constexpr (s == 0) {
-            rload<AMAJ, BM, 0, INSTR_A>(A, m0, nk * BK, rg);
-            rload<BMAJ, BN, 0, N_VMEM - INSTR_A>(B, n0, nk * BK, rg + INSTR_A);
-          }
-          if constexpr (s == NSTEP - 1) {
-            rstore<BM, 0, INSTR_A>(nstage, rg);
-            rstore<BN, 0, N_VMEM - INSTR_A>(nstage + A_BYTES / ES, rg + INSTR_A);
-          }
-        } else {
-          load_step<s>(A, B, m0, n0, nk * BK, nstage);
+    const int wm = wave_m(), wn = wave_n();
+    T* const nstage = lds + (cur ^ 1) * STAGE;
+    const T* as = lds + cur * STAGE;
+    const T* bs = lds + cur * STAGE + AOFF;
+    FragA fa[2][FM];
+    FragB fb[2][FN];
+    load_frags(as, bs, wm, wn, 0, fa[0], fb[0]);
+    u32x4_t rg[STAGING == STAGE_REG ? N_VMEM : 1];
+    static_for<NSTEP>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (STAGING == STAGE_REG) {
+        if constexpr (s == 0) {
+          rload<AMAJ, BM, 0, INSTR_A>(A, pm0, pk0, rg);
+          rload<BMAJ, BN, 0, N_VMEM - INSTR_A>(B, pn0, pk0, rg + INSTR_A);
         }
-        if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-        // Interleave this step's share of the next slice's global -> LDS copies
-        // and the next step's LDS reads with this step's MFMAs.
-        if constexpr (STAGING == STAGE_REG) {
-          if constexpr (s == 0) interleave<N_VMEM, 0x020>();
-        } else if constexpr (vmem_in_step(s) > 0) {
-          interleave<vmem_in_step(s), 0x020>();
+        if constexpr (s == NSTEP - 1) {
+          rstore<BM, 0, INSTR_A>(nstage, rg);
+          rstore<BN, 0, N_VMEM - INSTR_A>(nstage + AOFF, rg + INSTR_A);
         }
-        if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      } else {
+        load_step<s>(A, B, pm0, pn0, pk0, nstage);
+      }
+      if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+      if constexpr (STAGING == STAGE_REG) {
+        if constexpr (s == 0) interleave<N_VMEM, 0x020>();
+      } else if constexpr (vmem_in_step(s) > 0) {
+        interleave<vmem_in_step(s), 0x020>();
+      }
+      if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // Persistent main loop over a sequence of output tiles with K = K each:
+  // next(j, m0, n0) gives the origin of the j-th tile (false past the last one) and
+  // epi(acc, m0, n0) consumes a finished tile from registers (it may not use the
+  // LDS), after which acc restarts at zero.  The slices of all tiles form one
+  // stream through two LDS stages, so the first slice of tile j + 1 is copied
+  // while the last slice of tile j is multiplied and its epilogue runs.  Ends with
+  // a barrier: the caller may reuse the LDS afterwards.
+  template <class Next, class Epi>
+  static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
+                                                   Next&& next, Epi&& epi) {
+    static_assert(NSTAGE == 2, "the persistent loop double-buffers K slices");
+    constexpr int AOFF = A_BYTES / ES;
+    const int KT = (K + BK - 1) / BK;
+    int tm0, tn0;
+    if (!next(0, tm0, tn0)) return;
+    // copy cursor: slice pk of tile pj, origin (pm0, pn0); past the last tile it
+    // points at a K offset beyond every operand, so its copies read zeros
+    int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0;
+    bool pvalid = true;
+    load_tile<AMAJ, BM>(A, pm0, 0, lds);
+    load_tile<BMAJ, BN>(B, pn0, 0, lds + AOFF);
+    auto advance = [&]() {
+      if (++pk == KT) {
+        pk = 0;
+        ++pj;
+        pvalid = pvalid && next(pj, pm0, pn0);
+      }
+    };
+    advance();
+    zero(acc);
+    int q = 0;
+    for (int j = 0;;) {
+      for (int kt = 0; kt < KT; ++kt, ++q) {
+        wait_and_barrier<0>();
+        slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pk * BK : KT * BK, acc);
+        advance();
+      }
+      epi(acc, tm0, tn0);
+      if (!next(++j, tm0, tn0)) break;
+      zero(acc);
     }
-    // drain the trailing (all-zero) copies before the LDS is reused
     wait_and_barrier<0>();
+  }
+
+  // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T for a single tile.
+  static __device__ __forceinline__ void run(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int K,
+                                             T* lds, Acc& acc) {
+    run_tiles(
+        A, B, K, lds, acc,
+        [&](int j, int& tm, int& tn) {
+          tm = m0;
+          tn = n0;
+          return j == 0;
+        },
+        [](Acc&, int, int) {});
   }
 };
 
