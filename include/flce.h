@@ -129,6 +129,25 @@ flce_status flce_backward(const void* x, const void* W, const int64_t* target,
                           void* grad_W, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * Forward and backward in one call, for training steps that always need both
+ * (Liger-Kernel PR #928 thread: the gradients can be produced in the same call
+ * as the loss).  Same results, bit for bit, as flce_forward followed by
+ * flce_backward with the same arguments; the two phases share one workspace.
+ *
+ *   grad_loss   [1] float32 device scalar, or NULL for 1 (the gradient of loss
+ *               with respect to itself)
+ *   loss, lse   as for flce_forward; lse is also the backward's input
+ *   grad_x, grad_W  as for flce_backward
+ *   ws, ws_bytes    >= flce_forward_backward_workspace_bytes (smaller, down to the
+ *               backward's minimum plus 256 bytes, also works with smaller panels)
+ */
+size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
+flce_status flce_forward_backward(const void* x, const void* W, const int64_t* target, int64_t N,
+                                  int64_t H, int64_t V, flce_dtype dt, flce_reduction reduction,
+                                  const float* grad_loss, float* loss, float* lse, void* grad_x,
+                                  void* grad_W, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
  * Kernel timing, for benchmarks: the *_timed variants behave exactly like the
  * calls above and, in addition, record caller-created HIP events (hipEvent_t
  * handles passed as void*) on `hip_stream`: events[0] before the first kernel and
@@ -143,7 +162,8 @@ typedef enum {
   FLCE_K_FWD_LOSS = 2,    /* block sums -> scalar loss                             */
   FLCE_K_BWD_DLOGITS = 3, /* logit tile recompute -> dlogit panel                   */
   FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
-  FLCE_K_BWD_GRAD_X = 5   /* grad_x rows of one token chunk, one panel              */
+  FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel              */
+  FLCE_K_FILL = 6         /* writes the implicit grad_loss of 1                    */
 } flce_kernel;
 
 typedef struct {

@@ -25,7 +25,7 @@ _ESIZE = {F32: 4, BF16: 2}
 
 _lib = None
 
-KERNEL_NAMES = ["fwd_partial", "fwd_combine", "fwd_loss", "bwd_dlogits", "bwd_grad_w", "bwd_grad_x"]
+KERNEL_NAMES = ["fwd_partial", "fwd_combine", "fwd_loss", "bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "fill"]
 
 
 class Timing(ctypes.Structure):
@@ -70,7 +70,7 @@ def load() -> ctypes.CDLL:
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     for name in ("flce_forward_workspace_bytes", "flce_backward_workspace_bytes",
-                 "flce_backward_min_workspace_bytes"):
+                 "flce_backward_min_workspace_bytes", "flce_forward_backward_workspace_bytes"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, ctypes.c_int]
         fn.restype = sz
@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                   vp, vp, vp, sz, vp]
     lib.flce_backward.restype = ctypes.c_int
+    lib.flce_forward_backward.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp,
+                                          vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_forward_backward.restype = ctypes.c_int
     tp = ctypes.POINTER(Timing)
     lib.flce_forward_timed.argtypes = lib.flce_forward.argtypes + [tp]
     lib.flce_forward_timed.restype = ctypes.c_int
@@ -176,6 +179,35 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor, lse: t
     if code != 0:
         raise FLCEError(code)
     return gx, gW
+
+
+def forward_backward_workspace_bytes(N: int, H: int, V: int, dtype: torch.dtype) -> int:
+    return int(load().flce_forward_backward_workspace_bytes(N, H, V, _DT[dtype]))
+
+
+def flce_forward_backward(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor, reduction: str = "mean",
+                          grad_loss: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Return (loss [1] f32, lse [N] f32, grad_x, grad_W) from one library call."""
+    _check(x, W, target, reduction)
+    lib = load()
+    N, H = x.shape
+    V = W.shape[0]
+    dt = _DT[x.dtype]
+    loss = torch.empty(1, dtype=torch.float32, device=x.device)
+    lse = torch.empty(N, dtype=torch.float32, device=x.device)
+    gx = torch.empty_like(x)
+    gW = torch.empty_like(W)
+    gl = None
+    if grad_loss is not None:
+        gl = grad_loss.reshape(1).to(device=x.device, dtype=torch.float32).contiguous()
+    nws = lib.flce_forward_backward_workspace_bytes(N, H, V, dt)
+    ws = workspace if workspace is not None else torch.empty(nws, dtype=torch.uint8, device=x.device)
+    code = lib.flce_forward_backward(x.data_ptr(), W.data_ptr(), target.data_ptr(), N, H, V, dt, _RED[reduction],
+                                     gl.data_ptr() if gl is not None else None, loss.data_ptr(), lse.data_ptr(),
+                                     gx.data_ptr(), gW.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device))
+    if code != 0:
+        raise FLCEError(code)
+    return loss, lse, gx, gW
 
 
 class FLCEFunction(torch.autograd.Function):

@@ -214,6 +214,7 @@ flce_status flce_forward_timed(const void* x, const void* W, const int64_t* targ
   float* zt = target_logit ? target_logit : (float*)(base + p.off_zt);
   const double scale = reduction == FLCE_MEAN ? 1.0 / (double)N : 1.0;
   flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  rec.start();
   hipError_t e = flce::launch_forward((int)dt, p, x, W, target, (int)N, (int)H, (int)V, (float*)(base + p.off_m),
                                       (float*)(base + p.off_s), zt, lse, (double*)(base + p.off_blk), scale, loss,
                                       (hipStream_t)hip_stream, rec);
@@ -250,9 +251,56 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   char* base = (char*)ws;
   const float red_scale = reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f;
   flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  rec.start();
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
                                        (float*)(base + p.off_gw), (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  return 256 + std::max(plan_forward(N, V).total,
+                        plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total);
+}
+
+flce_status flce_forward_backward(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H,
+                                  int64_t V, flce_dtype dt, flce_reduction reduction, const float* grad_loss,
+                                  float* loss, float* lse, void* grad_x, void* grad_W, void* ws, size_t ws_bytes,
+                                  void* hip_stream) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (!loss || !lse || !grad_x || !grad_W) return FLCE_ERR_NULL;
+  const size_t es = esize(dt);
+  const Range in[4] = {{x, (size_t)N * H * es}, {W, (size_t)V * H * es}, {target, 8 * (size_t)N}, {grad_loss, 4}};
+  const Range out[4] = {{loss, 4}, {lse, 4 * (size_t)N}, {grad_x, (size_t)N * H * es}, {grad_W, (size_t)V * H * es}};
+  if (any_alias(in, 4, out, 4, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
+  // [0, 256): the implicit grad_loss; then one region the two phases share
+  // (the forward's partials are dead once its last kernel has run).
+  const FwdPlan fp = plan_forward(N, V);
+  BwdPlan bp;
+  if (!ws || ws_bytes < 256 + fp.total || !plan_backward(N, H, V, dt, ws_bytes - 256, &bp))
+    return FLCE_ERR_WORKSPACE;
+  bp.max_workgroups = flce::device_cu_count();
+  char* base = (char*)ws + 256;
+  hipStream_t s = (hipStream_t)hip_stream;
+  flce::Recorder rec{nullptr, s, hipSuccess};
+  const float* gl = grad_loss;
+  hipError_t e = hipSuccess;
+  if (!gl) {
+    e = flce::launch_fill((float*)ws, 1.0f, s, rec);
+    gl = (const float*)ws;
+  }
+  if (e == hipSuccess)
+    e = flce::launch_forward((int)dt, fp, x, W, target, (int)N, (int)H, (int)V, (float*)(base + fp.off_m),
+                             (float*)(base + fp.off_s), (float*)(base + fp.off_zt), lse,
+                             (double*)(base + fp.off_blk), reduction == FLCE_MEAN ? 1.0 / (double)N : 1.0, loss, s,
+                             rec);
+  if (e == hipSuccess)
+    e = flce::launch_backward((int)dt, bp, x, W, target, lse, gl,
+                              reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f, (int)N, (int)H, (int)V,
+                              grad_x, grad_W, base + bp.off_panel, (float*)(base + bp.off_gx),
+                              (float*)(base + bp.off_gw), s, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

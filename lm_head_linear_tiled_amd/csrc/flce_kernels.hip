@@ -399,9 +399,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   G::run_tiles(A, B, Kv, lds, acc, next, store);
 }
 
+__global__ void fill_scalar(float* p, float v) { p[0] = v; }
+
 // ---------------------------------------------------------------------------
 // Launchers (host side)
 // ---------------------------------------------------------------------------
+hipError_t launch_fill(float* p, float v, hipStream_t st, Recorder& rec) {
+  hipLaunchKernelGGL(fill_scalar, dim3(1), dim3(1), 0, st, p, v);
+  rec.after(FLCE_K_FILL);
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : rec.err;
+}
+
 template <typename T>
 static hipError_t launch_fwd_t(const FwdPlan& p, const void* x, const void* W, const int64_t* target, int N,
                                int H, int V, float* part_m, float* part_s, float* zt, float* lse, double* block_loss,

@@ -37,8 +37,12 @@ struct Recorder {
   flce_timing* t;
   hipStream_t s;
   hipError_t err;
+  bool started = false;
+  // Record events[0] once per library call (later phases of a combined call keep
+  // counting from where the previous one stopped).
   void start() {
-    if (t) {
+    if (t && !started) {
+      started = true;
       t->n_launches = 0;
       if (t->n_events > 0) record(t->events[0]);
     }
@@ -60,6 +64,8 @@ struct Recorder {
 hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W, const int64_t* target, int N,
                           int H, int V, float* part_m, float* part_s, float* zt, float* lse, double* block_loss,
                           double scale, float* loss, hipStream_t st, Recorder& rec);
+
+hipError_t launch_fill(float* p, float v, hipStream_t st, Recorder& rec);
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,

@@ -44,6 +44,9 @@ WORKLOADS = {
     "llama3_8k": Workload("llama3_8k", 8192, 4096, 128256, "bf16", ("mean",)),
     "llama3_16k": Workload("llama3_16k", 16384, 4096, 128256, "bf16", ("mean",)),
     "llama3_32k": Workload("llama3_32k", 32768, 4096, 128256, "bf16", ("mean",)),
+    # the other heads the Liger-Kernel PR #928 thread benchmarks
+    "qwen3_32k": Workload("qwen3_32k", 32768, 4096, 151936, "bf16", ("mean",)),
+    "gemma3_8k": Workload("gemma3_8k", 8192, 2304, 262208, "bf16", ("mean",)),
 }
 
 

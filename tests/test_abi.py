@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol(lib):
     names = binding.header_functions()
     assert set(names) >= {"flce_forward", "flce_backward", "flce_forward_workspace_bytes",
                           "flce_backward_workspace_bytes", "flce_backward_min_workspace_bytes",
-                          "flce_status_string"}
+                          "flce_status_string", "flce_forward_backward", "flce_forward_backward_workspace_bytes",
+                          "flce_forward_timed", "flce_backward_timed"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -108,3 +109,28 @@ def test_binding_refuses_cpu_tensors():
         binding.flce_forward(x, torch.zeros(5, 8), torch.zeros(4, dtype=torch.int64))
     with pytest.raises(TypeError):
         binding.flce_forward(x.double(), torch.zeros(5, 8).double(), torch.zeros(4, dtype=torch.int64))
+
+
+def fb(lib, x=X, W=Wp, t=T, N=64, H=128, V=1000, dt=F32, red=MEAN, gl=GL, loss=LOSS, lse=LSE, gx=GX, gw=GW,
+       ws=WSP, nws=None):
+    if nws is None:
+        nws = lib.flce_forward_backward_workspace_bytes(N, H, V, dt) if N > 0 and H > 0 and V > 0 else 0
+    return lib.flce_forward_backward(x, W, t, N, H, V, dt, red, gl, loss, lse, gx, gw, ws, nws, None)
+
+
+def test_forward_backward_rejects(lib):
+    assert fb(lib, x=None) == NULL
+    assert fb(lib, lse=None) == NULL
+    assert fb(lib, gw=None) == NULL
+    assert fb(lib, N=0) == SHAPE
+    assert fb(lib, dt=4) == DTYPE
+    assert fb(lib, red=3) == RED
+    assert fb(lib, W=Wp + 8) == ALIGN
+    assert fb(lib, lse=GX + 32) == ALIAS       # lse inside grad_x
+    assert fb(lib, gl=LOSS) == ALIAS           # grad_loss is the loss output
+    assert fb(lib, ws=X) == ALIAS
+    assert fb(lib, ws=None) == WS
+    assert fb(lib, nws=255) == WS
+    n = lib.flce_forward_backward_workspace_bytes(64, 128, 1000, F32)
+    assert n >= 256 + lib.flce_forward_workspace_bytes(64, 128, 1000, F32)
+    assert n >= 256 + lib.flce_backward_workspace_bytes(64, 128, 1000, F32)

@@ -24,7 +24,7 @@ FULL_ORACLE_FLOP = 9e12  # full float64 forward on the host: ~10 s at ~1 TFLOP/s
 
 
 @pytest.mark.parametrize("name", ["llama3_4k", "llama2_4k", "llama2_32k", "llama3_8k", "llama3_16k",
-                                  "llama3_32k"])
+                                  "llama3_32k", "qwen3_32k", "gemma3_8k"])
 def test_full_size(gpu, name):
     w = WORKLOADS[name]
     N, H, V, dt = w.N, w.H, w.V, w.dtype

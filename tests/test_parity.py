@@ -171,3 +171,43 @@ def test_autograd_matches_direct(gpu):
     got = run_hip(gpu, x, W, t, "bf16", "mean", grad_loss=2.0)
     assert loss.item() == got["loss"]
     assert np.array_equal(to_f64(xd.grad), got["gx"]) and np.array_equal(to_f64(Wd.grad), got["gW"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_grad_loss", [False, True])
+def test_forward_backward_single_call(gpu, dtype, with_grad_loss):
+    """One call gives the same bits as flce_forward then flce_backward."""
+    N, H, V = 700, 96, 1500
+    note(f"[parity] single call {dtype} grad_loss={with_grad_loss}")
+    x, W, t = make_inputs(N, H, V, dtype, seed=14)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    gl = torch.tensor([0.75 if with_grad_loss else 1.0], device="cuda")
+    loss, lse, gx, gW = gpu.flce_forward_backward(xd, Wd, td, "sum", grad_loss=gl if with_grad_loss else None)
+    l2, lse2 = gpu.flce_forward(xd, Wd, td, "sum")
+    gx2, gW2 = gpu.flce_backward(xd, Wd, td, lse2, gl, "sum")
+    torch.cuda.synchronize()
+    assert torch.equal(loss, l2) and torch.equal(lse, lse2)
+    assert torch.equal(gx, gx2) and torch.equal(gW, gW2)
+    # and against the oracle
+    ref = oracle_all(x, W, t, dtype, "sum", float(gl.item()))
+    got = dict(loss=float(loss.item()), lse=to_f64(lse), zt=None, gx=to_f64(gx), gW=to_f64(gW))
+    assert_parity(got, ref[0], None, None, ref[3], ref[4], dtype)
+
+
+def test_timed_variants_record_every_kernel(gpu):
+    """The *_timed calls give the same bits as the plain calls and one event per kernel."""
+    N, H, V = 300, 128, 2000
+    x, W, t = make_inputs(N, H, V, "bf16", seed=15)
+    xd, Wd, td = to_dev(x, "bf16"), to_dev(W, "bf16"), torch.from_numpy(t).cuda()
+    ft, bt = gpu.KernelTimer(8), gpu.KernelTimer(64)
+    l1, lse1 = gpu.flce_forward(xd, Wd, td, "mean", timer=ft)
+    gx1, gW1 = gpu.flce_backward(xd, Wd, td, lse1, torch.ones(1, device="cuda"), "mean", timer=bt)
+    l2, lse2 = gpu.flce_forward(xd, Wd, td, "mean")
+    gx2, gW2 = gpu.flce_backward(xd, Wd, td, lse2, torch.ones(1, device="cuda"), "mean")
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(gx1, gx2) and torch.equal(gW1, gW2)
+    fk = [k for k, _ in ft.durations()]
+    assert fk == ["fwd_partial", "fwd_combine", "fwd_loss"]
+    bk = [k for k, _ in bt.durations()]
+    assert len(bk) % 3 == 0 and bk[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"]
+    assert all(ms >= 0 for _, ms in ft.durations() + bt.durations())
