@@ -284,6 +284,38 @@ struct TileGemm {
                       : 0;
   }
 
+  // One scheduling pattern per fragment step: after each of the step's N_MFMA
+  // MFMAs, first up to two of the NR LDS reads (the next step's fragments, so they
+  // are in flight as early as possible), then, once those are placed, the NV
+  // global loads / DMA copies and the NW LDS writes spread over the remaining MFMAs.
+  template <int NR, int NV, int NW>
+  static __device__ __forceinline__ void schedule_step() {
+    constexpr int RPER = 2;
+    constexpr int QR = (NR + RPER - 1) / RPER;              // MFMA slots taken by the reads
+    constexpr int REST = N_MFMA - QR > 0 ? N_MFMA - QR : 1;  // slots left for the rest
+    constexpr int VPER_ = (NV + REST - 1) / REST;
+    constexpr int WPER_ = (NW + REST - 1) / REST;
+    static_for<N_MFMA>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int r = NR - RPER * q < RPER ? (NR - RPER * q > 0 ? NR - RPER * q : 0) : RPER;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+      constexpr int k = q - QR;  // index among the remaining slots
+      if constexpr (k >= 0) {
+        constexpr int v = NV - VPER_ * k < VPER_ ? (NV - VPER_ * k > 0 ? NV - VPER_ * k : 0) : VPER_;
+        constexpr int w = NW - WPER_ * k < WPER_ ? (NW - WPER_ * k > 0 ? NW - WPER_ * k : 0) : WPER_;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+      }
+    });
+    // anything that did not fit (fewer MFMAs than reads) goes last
+    constexpr int RLEFT = NR - RPER * N_MFMA > 0 ? NR - RPER * N_MFMA : 0;
+    if constexpr (RLEFT > 0) __builtin_amdgcn_sched_group_barrier(0x100, RLEFT, 0);
+    constexpr int VLEFT = N_MFMA <= QR ? NV : 0, WLEFT = N_MFMA <= QR ? NW : 0;
+    if constexpr (VLEFT > 0) __builtin_amdgcn_sched_group_barrier(0x020, VLEFT, 0);
+    if constexpr (WLEFT > 0) __builtin_amdgcn_sched_group_barrier(0x200, WLEFT, 0);
+  }
+
   // Scheduling groups: spread NI instructions of class MASK evenly between the
   // N_MFMA MFMAs of one step.
   template <int NI, int MASK>
@@ -365,12 +397,11 @@ struct TileGemm {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-      if constexpr (STAGING == STAGE_REG) {
-        if constexpr (s == 0) interleave<N_VMEM, 0x020>();
-      } else if constexpr (vmem_in_step(s) > 0) {
-        interleave<vmem_in_step(s), 0x020>();
-      }
-      if constexpr (s + 1 < NSTEP) interleave<N_DS, 0x100>();
+      constexpr int NR = s + 1 < NSTEP ? N_DS : 0;
+      if constexpr (STAGING == STAGE_REG)
+        schedule_step<NR, s == 0 ? N_VMEM : 0, s == NSTEP - 1 ? N_VMEM : 0>();
+      else
+        schedule_step<NR, vmem_in_step(s), 0>();
       __builtin_amdgcn_sched_barrier(0);
     });
   }
