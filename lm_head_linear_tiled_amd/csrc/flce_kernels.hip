@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
     tn0 = n0;
     return vt_begin + j < vt_end;
   };
-  auto fold = [&](typename G::Acc& a, int m0, int) {
+  auto fold = [&](typename G::Acc& a, int m0, int, char*) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       float tmax = -INFINITY;
@@ -257,48 +257,110 @@ __device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n,
   return true;
 }
 
+// Four consecutive float outputs as 4 elements of T (bfloat16: hardware
+// round-to-nearest-even conversion), and the 16-byte LDS accesses of the
+// dlogit staging below.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){a, b}, bf16x2v_t));
+}
+
+// Sᵀ tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major), as
+// in the forward, so lse and target are read once per token column.  The D
+// tile goes to the panel [token][vocabulary] through the spare LDS stage: each
+// wave owns 8 KiB of it, writes its 64-entry vocabulary span for a round of
+// tokens (four consecutive vocabulary entries per lane and accumulator group),
+// reads the rows back 16 bytes per lane and stores whole 128-byte lines.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
                                                         const int64_t* __restrict__ target,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ grad_loss, float red_scale, int N,
-                                                        int H, int V, int i0, int v0, int tiles_m, int tiles_n,
+                                                        int H, int V, int i0, int v0, int tiles_v, int tiles_t,
                                                         int Vbp, T* __restrict__ panel) {
-  // S tile: rows = tokens (A = x, K-major), cols = vocabulary (B = W, K-major).
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
+  static_assert(G::WM == 64 && G::STAGE_BYTES >= G::NWAVES * 8192, "dlogit staging layout");
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-  const Operand<T> A{x, H, N, H};
-  const Operand<T> B{W, H, V, H};
+  const Operand<T> A{W, H, V, H};
+  const Operand<T> B{x, H, N, H};
   const float s = grad_loss[0] * red_scale;
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
-    m0 = i0 + tm * kTile;
-    n0 = v0 + tn * kTile;
+    if (!persistent_tile(j, tiles_v, tiles_t, tm, tn)) return false;
+    m0 = v0 + tm * kTile;
+    n0 = i0 + tn * kTile;
     return true;
   };
-  auto store = [&](typename G::Acc& acc, int m0, int n0) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int RB = 64 * (int)sizeof(T);  // bytes of one token row of a wave's vocabulary span
+  constexpr int TR = 8192 / RB;            // tokens per round: 64 (bf16) or 32 (fp32)
+  constexpr int JR = TR / 32;              // accumulator column blocks per round
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
+    char* sc = spare + ((int)threadIdx.x >> 6) * 8192;
+    const int vw = m0 + wm * G::WM;  // first vocabulary row of this wave
+    // every wave has read its last fragments from spare (the copies still in
+    // flight go to the other stage, so no vmcnt wait here)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < G::FM; ++i)
+    for (int rd = 0; rd < G::FN / JR; ++rd) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-        const bool rv = row < N;
-        const float lr = rv ? lse[row] * kLog2e : 0.f;
-        const int64_t tr = rv ? target[row] : -1;
+      for (int jj = 0; jj < JR; ++jj) {
+        const int j = rd * JR + jj;
+        const int tl = jj * 32 + (l & 31);  // token row within the round
+        const int tok = n0 + wn * G::WN + j * 32 + (l & 31);
+        const bool tv = tok < N;
+        const float lr = tv ? lse[tok] * kLog2e : 0.f;
+        const int64_t tt = tv ? target[tok] : -1;
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j) {
-          const int col = n0 + wn * G::WN + j * 32 + (l & 31);
-          float d = 0.f;
-          if (rv && col < V) {
-            const float p = __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - lr);
-            d = s * (p - (col == tr ? 1.f : 0.f));
+        for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int vl = i * 32 + 8 * g + 4 * (l >> 5);  // entries vl .. vl + 3 of the span
+            float d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int v = vw + vl + u;
+              d[u] = 0.f;
+              if (tv && v < V) {
+                const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr);
+                d[u] = s * (p - (v == tt ? 1.f : 0.f));
+              }
+            }
+            if constexpr (BF) {
+              // 8-byte half of 16-byte slot: slot ^ (tl/2 % 8), half ^ (tl/16 % 2), so the
+              // 32 lanes of a write phase (tl = 0..31) hit 32 distinct bank pairs
+              const int slot = (vl >> 3) ^ ((tl >> 1) & 7);
+              const int half = ((vl >> 2) & 1) ^ ((tl >> 4) & 1);
+              *reinterpret_cast<uint2*>(sc + tl * RB + slot * 16 + half * 8) =
+                  make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+            } else {
+              const int slot = (vl >> 2) ^ (tl & 15);
+              *reinterpret_cast<float4*>(sc + tl * RB + slot * 16) = make_float4(d[0], d[1], d[2], d[3]);
+            }
           }
-          panel[(int64_t)(row - i0) * Vbp + (col - v0)] = from_f32<T>(d);
-        }
       }
+      // rows back, 16 bytes per lane, whole rows per group of lanes
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        int row, k;
+        uint4 v;
+        if constexpr (BF) {
+          row = q * 8 + (l >> 3);
+          k = l & 7;
+          v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
+          if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        } else {
+          row = q * 4 + (l >> 4);
+          k = l & 15;
+          v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ (row & 15)) * 16));
+        }
+        const int tok = n0 + wn * G::WN + rd * TR + row;
+        *reinterpret_cast<uint4*>(panel + (int64_t)(tok - i0) * Vbp + (vw - v0) + k * (16 / (int)sizeof(T))) = v;
+      }
+    }
   };
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);
@@ -326,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
     return true;
   };
   // gw_out and gw_acc point at row v0 of their buffers; rows are panel-local.
-  auto store = [&](typename G::Acc& acc, int m0, int n0) {
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char*) {
 #pragma unroll
     for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -372,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
     n0 = tn * kTile;
     return true;
   };
-  auto store = [&](typename G::Acc& acc, int m0, int n0) {
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char*) {
 #pragma unroll
     for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -466,7 +528,7 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int tiles_n = (Kv + kTile - 1) / kTile;
       auto grid = [&](int tiles) { return dim3(min(tiles, p.max_workgroups)); };
       hipLaunchKernelGGL(bwd_dlogits<T>, grid(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
-                         red_scale, N, H, V, i0, v0, tiles_m, tiles_n, Vbp, panel);
+                         red_scale, N, H, V, i0, v0, tiles_n, tiles_m, Vbp, panel);
       rec.after(FLCE_K_BWD_DLOGITS);
       // grad_W rows of this panel accumulate over token chunks.
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;

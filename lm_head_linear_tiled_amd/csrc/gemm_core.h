@@ -408,11 +408,15 @@ struct TileGemm {
 
   // Persistent main loop over a sequence of output tiles with K = K each:
   // next(j, m0, n0) gives the origin of the j-th tile (false past the last one) and
-  // epi(acc, m0, n0) consumes a finished tile from registers (it may not use the
-  // LDS), after which acc restarts at zero.  The slices of all tiles form one
-  // stream through two LDS stages, so the first slice of tile j + 1 is copied
-  // while the last slice of tile j is multiplied and its epilogue runs.  Ends with
-  // a barrier: the caller may reuse the LDS afterwards.
+  // epi(acc, m0, n0, spare) consumes a finished tile, after which acc restarts at
+  // zero.  The slices of all tiles form one stream through two LDS stages, so the
+  // first slice of tile j + 1 is copied while the last slice of tile j is
+  // multiplied and its epilogue runs.  spare is the stage that last slice was
+  // read from: an epilogue may use its STAGE_BYTES after a workgroup barrier
+  // (other waves may still be reading their last fragments from it) and until
+  // it returns (the next slice's copies into it start after the barrier that
+  // opens that slice).  Every wave of the workgroup calls epi for the same tiles.
+  // Ends with a barrier: the caller may reuse the LDS afterwards.
   template <class Next, class Epi>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
                                                    Next&& next, Epi&& epi) {
@@ -443,7 +447,7 @@ struct TileGemm {
         slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pk * BK : KT * BK, acc);
         advance();
       }
-      epi(acc, tm0, tn0);
+      epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
       if (!next(++j, tm0, tn0)) break;
       zero(acc);
     }
@@ -460,7 +464,7 @@ struct TileGemm {
           tn = n0;
           return j == 0;
         },
-        [](Acc&, int, int) {});
+        [](Acc&, int, int, char*) {});
   }
 };
 
