@@ -266,12 +266,91 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){a, b}, bf16x2v_t));
 }
 
+// Tile epilogue through the spare LDS stage.  A wave's 64 x 128 accumulator
+// sub-tile (M side: four consecutive rows per lane and accumulator group; N side:
+// one column per lane) is written to 8 KiB of LDS per wave, a round of N columns
+// at a time, and read back so that each lane holds 16 contiguous bytes of one
+// output row n, along which M is contiguous in memory: the global accesses then
+// cover whole 128-byte lines.
+//   val(i, j, g, d): d[0..3] = values of rows 32 i + 8 g + 4 (l / 32) + 0..3 and
+//                    column 32 j + l % 32 of the sub-tile (l: lane)
+//   out(n, m, v):    n in [0, 128), m in [0, 64) a multiple of 16 / sizeof(S),
+//                    v = 16 bytes: elements m .. of row n, as S
+// LDS slots are XOR-swizzled so that the writes (32 lanes of different n) and the
+// reads (whole rows) are free of bank conflicts.  Starts with a workgroup barrier.
+template <typename S, int FM, int FN, class Val, class Out>
+__device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& out) {
+  static_assert(FM == 2 && FN == 4, "64 x 128 wave sub-tile");
+  constexpr bool BF = sizeof(S) == 2;
+  constexpr int RB = 64 * (int)sizeof(S);  // bytes of one output row of the sub-tile
+  constexpr int TR = 8192 / RB;            // rows per round: 64 (bf16) or 32 (fp32)
+  constexpr int JR = TR / 32;              // accumulator column blocks per round
+  const int l = (int)threadIdx.x & 63;
+  char* sc = spare + ((int)threadIdx.x >> 6) * 8192;
+  // every wave has read its last fragments from spare (the copies still in flight
+  // go to the other stage, so no vmcnt wait here)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int rd = 0; rd < FN / JR; ++rd) {
+#pragma unroll
+    for (int jj = 0; jj < JR; ++jj) {
+      const int tl = jj * 32 + (l & 31);  // row of the round
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ml = i * 32 + 8 * g + 4 * (l >> 5);  // elements ml .. ml + 3 of the row
+          float d[4];
+          val(i, rd * JR + jj, g, d);
+          if constexpr (BF) {
+            // 8-byte half of a 16-byte slot: slot ^ (tl/2 % 8), half ^ (tl/16 % 2)
+            const int slot = (ml >> 3) ^ ((tl >> 1) & 7);
+            const int half = ((ml >> 2) & 1) ^ ((tl >> 4) & 1);
+            *reinterpret_cast<uint2*>(sc + tl * RB + slot * 16 + half * 8) =
+                make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+          } else {
+            const int slot = (ml >> 2) ^ (tl & 15);
+            *reinterpret_cast<float4*>(sc + tl * RB + slot * 16) = make_float4(d[0], d[1], d[2], d[3]);
+          }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int row, k;
+      uint4 v;
+      if constexpr (BF) {
+        row = q * 8 + (l >> 3);
+        k = l & 7;
+        v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
+        if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      } else {
+        row = q * 4 + (l >> 4);
+        k = l & 15;
+        v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ (row & 15)) * 16));
+      }
+      out(rd * TR + row, k * (16 / (int)sizeof(S)), v);
+    }
+  }
+}
+
+// 16 bytes holding four floats, added to the four floats at p; returns the sums.
+__device__ __forceinline__ float4 add4(uint4 v, const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  return make_float4(__uint_as_float(v.x) + a.x, __uint_as_float(v.y) + a.y, __uint_as_float(v.z) + a.z,
+                     __uint_as_float(v.w) + a.w);
+}
+__device__ __forceinline__ float4 as_float4(uint4 v) {
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+// Four floats stored as T at p (bfloat16: round to nearest even).
+__device__ __forceinline__ void store_out4(bf16_t* p, float4 f) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
+}
+__device__ __forceinline__ void store_out4(float* p, float4 f) { *reinterpret_cast<float4*>(p) = f; }
+
 // Sᵀ tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major), as
-// in the forward, so lse and target are read once per token column.  The D
-// tile goes to the panel [token][vocabulary] through the spare LDS stage: each
-// wave owns 8 KiB of it, writes its 64-entry vocabulary span for a round of
-// tokens (four consecutive vocabulary entries per lane and accumulator group),
-// reads the rows back 16 bytes per lane and stores whole 128-byte lines.
+// in the forward, so lse and target are read once per token column; the D tile
+// reaches the panel [token][vocabulary] through the staged epilogue.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x, const T* __restrict__ W,
                                                         const int64_t* __restrict__ target,
@@ -294,168 +373,131 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
     n0 = i0 + tn * kTile;
     return true;
   };
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int RB = 64 * (int)sizeof(T);  // bytes of one token row of a wave's vocabulary span
-  constexpr int TR = 8192 / RB;            // tokens per round: 64 (bf16) or 32 (fp32)
-  constexpr int JR = TR / 32;              // accumulator column blocks per round
   auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    char* sc = spare + ((int)threadIdx.x >> 6) * 8192;
     const int vw = m0 + wm * G::WM;  // first vocabulary row of this wave
-    // every wave has read its last fragments from spare (the copies still in
-    // flight go to the other stage, so no vmcnt wait here)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int tw = n0 + wn * G::WN;  // first token of this wave
+    // lse (log2 units) and target of this lane's token in each column block; a
+    // target outside [0, V) gets no one-hot term
+    float lr[G::FN];
+    int tt[G::FN];
+    bool tv[G::FN];
 #pragma unroll
-    for (int rd = 0; rd < G::FN / JR; ++rd) {
+    for (int j = 0; j < G::FN; ++j) {
+      const int tok = tw + j * 32 + (l & 31);
+      tv[j] = tok < N;
+      const int64_t t64 = tv[j] ? target[tok] : -1;
+      lr[j] = tv[j] ? lse[tok] * kLog2e : 0.f;
+      tt[j] = t64 >= 0 && t64 < V ? (int)t64 : -1;
+    }
+    staged_epilogue<T, G::FM, G::FN>(
+        spare,
+        [&](int i, int j, int g, float* d) {
 #pragma unroll
-      for (int jj = 0; jj < JR; ++jj) {
-        const int j = rd * JR + jj;
-        const int tl = jj * 32 + (l & 31);  // token row within the round
-        const int tok = n0 + wn * G::WN + j * 32 + (l & 31);
-        const bool tv = tok < N;
-        const float lr = tv ? lse[tok] * kLog2e : 0.f;
-        const int64_t tt = tv ? target[tok] : -1;
-#pragma unroll
-        for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int vl = i * 32 + 8 * g + 4 * (l >> 5);  // entries vl .. vl + 3 of the span
-            float d[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int v = vw + vl + u;
-              d[u] = 0.f;
-              if (tv && v < V) {
-                const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr);
-                d[u] = s * (p - (v == tt ? 1.f : 0.f));
-              }
-            }
-            if constexpr (BF) {
-              // 8-byte half of 16-byte slot: slot ^ (tl/2 % 8), half ^ (tl/16 % 2), so the
-              // 32 lanes of a write phase (tl = 0..31) hit 32 distinct bank pairs
-              const int slot = (vl >> 3) ^ ((tl >> 1) & 7);
-              const int half = ((vl >> 2) & 1) ^ ((tl >> 4) & 1);
-              *reinterpret_cast<uint2*>(sc + tl * RB + slot * 16 + half * 8) =
-                  make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-            } else {
-              const int slot = (vl >> 2) ^ (tl & 15);
-              *reinterpret_cast<float4*>(sc + tl * RB + slot * 16) = make_float4(d[0], d[1], d[2], d[3]);
+          for (int u = 0; u < 4; ++u) {
+            const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
+            d[u] = 0.f;
+            if (tv[j] && v < V) {
+              const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr[j]);
+              d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
             }
           }
-      }
-      // rows back, 16 bytes per lane, whole rows per group of lanes
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        int row, k;
-        uint4 v;
-        if constexpr (BF) {
-          row = q * 8 + (l >> 3);
-          k = l & 7;
-          v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
-          if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        } else {
-          row = q * 4 + (l >> 4);
-          k = l & 15;
-          v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ (row & 15)) * 16));
-        }
-        const int tok = n0 + wn * G::WN + rd * TR + row;
-        *reinterpret_cast<uint4*>(panel + (int64_t)(tok - i0) * Vbp + (vw - v0) + k * (16 / (int)sizeof(T))) = v;
-      }
-    }
+        },
+        [&](int n, int m, uint4 v) {
+          *reinterpret_cast<uint4*>(panel + (int64_t)(tw + n - i0) * Vbp + (vw - v0) + m) = v;
+        });
   };
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);
 }
 
-// grad_W[v0 + m, h] for m in the panel: A = panel as [k = token][m = vocab]
-// (MN-major), B = x rows i0.. as [k = token][n = hidden] (MN-major).
+// Final or accumulated output of a backward contraction through the staged
+// epilogue: out rows are the N side of the tile (row_ok tells which exist and
+// row_off gives their element offset), M (hidden) is contiguous.
+//   accumulate: add the float32 partial sums in acc_buf first
+//   final:      write T to dst, else float32 to acc_buf
+// A tile that is neither accumulated nor kept in float32 stages T directly.
+template <typename T, class G, class RowOk, class RowOff>
+__device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare, int hw, int nw, int H,
+                                              int accumulate, int final, T* __restrict__ dst,
+                                              float* __restrict__ acc_buf, RowOk&& row_ok, RowOff&& row_off) {
+  auto val = [&](int i, int j, int g, float* d) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] = acc[i][j][4 * g + u];
+  };
+  if (!accumulate && final) {
+    staged_epilogue<T, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
+      if (!row_ok(nw + n) || hw + m >= H) return;
+      *reinterpret_cast<uint4*>(dst + row_off(nw + n) + hw + m) = v;
+    });
+  } else {
+    staged_epilogue<float, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
+      if (!row_ok(nw + n) || hw + m >= H) return;
+      const int64_t o = row_off(nw + n) + hw + m;
+      const float4 f = accumulate ? add4(v, acc_buf + o) : as_float4(v);
+      if (final)
+        store_out4(dst + o, f);
+      else
+        *reinterpret_cast<float4*>(acc_buf + o) = f;
+    });
+  }
+}
+
+// grad_Wᵀ tile of the panel: rows = hidden (A = x rows i0.. as [k = token][m =
+// hidden], MN-major), cols = panel vocabulary (B = the panel as [k = token][n =
+// vocabulary], MN-major); written as grad_W rows v0 + n, hidden contiguous.
+// gw_out and gw_acc point at row v0 of their buffers.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
                                                        const T* __restrict__ x, int H, int V, int i0, int v0,
-                                                       int Vb, int tiles_m, int tiles_n, T* __restrict__ gw_out,
+                                                       int Vb, int tiles_h, int tiles_v, T* __restrict__ gw_out,
                                                        float* __restrict__ gw_acc, int accumulate, int final) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-  const Operand<T> A{panel, Vbp, Vbp, Kc};
-  const Operand<T> B{x + (int64_t)i0 * H, H, H, Kc};
+  const Operand<T> A{x + (int64_t)i0 * H, H, H, Kc};
+  const Operand<T> B{panel, Vbp, Vbp, Kc};
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
+    if (!persistent_tile(j, tiles_h, tiles_v, tm, tn)) return false;
     m0 = tm * kTile;
     n0 = tn * kTile;
     return true;
   };
-  // gw_out and gw_acc point at row v0 of their buffers; rows are panel-local.
-  auto store = [&](typename G::Acc& acc, int m0, int n0, char*) {
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-        if (m >= Vb || v0 + m >= V) continue;
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j) {
-          const int h = n0 + wn * G::WN + j * 32 + (l & 31);
-          if (h >= H) continue;
-          const int64_t o = (int64_t)m * H + h;
-          float val = acc[i][j][r];
-          if (accumulate) val += gw_acc[o];
-          if (final)
-            gw_out[o] = from_f32<T>(val);
-          else
-            gw_acc[o] = val;
-        }
-      }
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
+    grad_epilogue<T, G>(
+        acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, final, gw_out, gw_acc,
+        [&](int v) { return v < Vb && v0 + v < V; }, [&](int v) { return (int64_t)v * H; });
   };
   typename G::Acc acc;
   G::run_tiles(A, B, Kc, lds, acc, next, store);
 }
 
-// grad_x[i0 + m, h]: A = panel as [m = token][k = vocab] (K-major), B = W rows
-// v0.. as [k = vocab][n = hidden] (MN-major).
+// grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
+// vocabulary][m = hidden], MN-major), cols = chunk tokens (B = the panel as [n =
+// token][k = vocabulary], K-major); written as grad_x rows i0 + n.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
                                                        const T* __restrict__ W, int H, int N, int i0, int v0,
-                                                       int tiles_m, int tiles_n, T* __restrict__ gx_out,
+                                                       int tiles_h, int tiles_t, T* __restrict__ gx_out,
                                                        float* __restrict__ gx_acc, int accumulate, int final) {
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
-  const Operand<T> A{panel, Vbp, Kc, Vbp};
-  const Operand<T> B{W + (int64_t)v0 * H, H, H, Kv};
+  const Operand<T> A{W + (int64_t)v0 * H, H, H, Kv};
+  const Operand<T> B{panel, Vbp, Kc, Vbp};
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_m, tiles_n, tm, tn)) return false;
+    if (!persistent_tile(j, tiles_h, tiles_t, tm, tn)) return false;
     m0 = tm * kTile;
     n0 = tn * kTile;
     return true;
   };
-  auto store = [&](typename G::Acc& acc, int m0, int n0, char*) {
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-        if (m >= Kc) continue;
-        const int row = i0 + m;
-        if (row >= N) continue;
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j) {
-          const int h = n0 + wn * G::WN + j * 32 + (l & 31);
-          if (h >= H) continue;
-          const int64_t o = (int64_t)row * H + h;
-          float val = acc[i][j][r];
-          if (accumulate) val += gx_acc[o];
-          if (final)
-            gx_out[o] = from_f32<T>(val);
-          else
-            gx_acc[o] = val;
-        }
-      }
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
+    grad_epilogue<T, G>(
+        acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, final, gx_out, gx_acc,
+        [&](int t) { return t < Kc && i0 + t < N; }, [&](int t) { return (int64_t)(i0 + t) * H; });
   };
   typename G::Acc acc;
   G::run_tiles(A, B, Kv, lds, acc, next, store);
@@ -533,12 +575,12 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       // grad_W rows of this panel accumulate over token chunks.
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
       hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
-                         V, i0, v0, Kv, tiles_n, tiles_h, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
+                         V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
                          c == p.n_chunks - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_W);
       // grad_x rows of this chunk accumulate over vocabulary panels.
       hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, Kv, W,
-                         H, N, i0, v0, tiles_m, tiles_h, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
+                         H, N, i0, v0, tiles_h, tiles_m, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_X);
     }
   }
