@@ -30,6 +30,10 @@ def parse():
     ap.add_argument("--workload", default="llama3_4k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", choices=["panels", "chunked"], default="panels",
+                    help="panels: flce_backward (bounded dlogit panels, the default); chunked: "
+                         "flce_backward_chunked, token chunks over the whole vocabulary, for comparison")
+    ap.add_argument("--chunk-tokens", type=int, default=1024, help="tokens per chunk for --backward chunked")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), to scale the HBM counters")
     return ap.parse_args()
@@ -141,13 +145,21 @@ def main():
     td = torch.from_numpy(t).to(dev)
     gl = torch.ones(1, dtype=torch.float32, device=dev)
     fws = torch.empty(binding.forward_workspace_bytes(N, H, V, tdt), dtype=torch.uint8, device=dev)
-    bws = torch.empty(binding.backward_workspace_bytes(N, H, V, tdt), dtype=torch.uint8, device=dev)
+    if args.backward == "chunked":
+        nbws = binding.backward_chunked_workspace_bytes(N, H, V, tdt, args.chunk_tokens)
+    else:
+        nbws = binding.backward_workspace_bytes(N, H, V, tdt)
+    bws = torch.empty(nbws, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
     def step(ft=None, bt=None):
         loss, lse = binding.flce_forward(xd, Wd, td, red, workspace=fws, timer=ft)
-        gx, gW = binding.flce_backward(xd, Wd, td, lse, gl, red, workspace=bws, timer=bt)
+        if args.backward == "chunked":
+            gx, gW = binding.flce_backward_chunked(xd, Wd, td, lse, gl, red, chunk_tokens=args.chunk_tokens,
+                                                   workspace=bws, timer=bt)
+        else:
+            gx, gW = binding.flce_backward(xd, Wd, td, lse, gl, red, workspace=bws, timer=bt)
         return loss, gx, gW
 
     for _ in range(args.warmup):
@@ -203,7 +215,8 @@ def main():
     total_flops = roofline.fwdbwd_flops(N, H, V)
     value = total_flops / (ms_step * 1e-3) / 1e12
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "llama3_4k" else
+        f"fwd+bwd ms & TFLOP/s (8NHV) at V={V} H={H} N={N} {dtype}; fwd ms",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -215,8 +228,10 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (x~N(0,1), W~N(0,1/sqrt(H)), targets uniform, seed 0)",
-        "config": {"workload": f"llama3 head V={V} H={H} N={N} {dtype} mean, forward+backward",
-                   "N": N, "H": H, "V": V, "reduction": red},
+        "config": {"workload": f"{args.workload}: LM head V={V} H={H} N={N} {dtype} mean, forward+backward",
+                   "N": N, "H": H, "V": V, "reduction": red,
+                   "backward": "panels" if args.backward == "panels" else f"chunked {args.chunk_tokens} tokens",
+                   "backward_workspace_bytes": int(nbws)},
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(roofline.fwd_flops(N, H, V) / (fwd_ms * 1e-3) / 1e12, 2),
         "fwdbwd_frac_of_peak": round(value / peak, 4),

@@ -184,6 +184,31 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
                                 void* grad_W, void* ws, size_t ws_bytes, void* hip_stream,
                                 flce_timing* timing);
 
+/*
+ * Token-chunked backward, for comparison with flce_backward's bounded panels.
+ * Source: Liger-Kernel PR #928 thread, where the author replaces the fully fused
+ * backward by a chunk backward that recomputes the logits of one chunk of tokens
+ * over the whole vocabulary and then accumulates the input and weight gradients.
+ * Arguments and results (up to rounding order) as for flce_backward_timed, plus
+ *
+ *   chunk_tokens  tokens per chunk, >= 1 (FLCE_ERR_SHAPE otherwise); rounded up to
+ *                 a multiple of 256 and capped at N rounded up to 256.  Each
+ *                 chunk's dlogits [chunk, V] go to the workspace; grad_x rows of
+ *                 the chunk come from one contraction over V; grad_W is summed
+ *                 over the chunks (through a float32 [V, H] buffer in the
+ *                 workspace for bfloat16, in place for float32).
+ *   ws, ws_bytes  >= flce_backward_chunked_workspace_bytes(N, H, V, dt, chunk_tokens)
+ *                 (0 for invalid arguments); no smaller-panel fallback
+ *   timing        as for the *_timed variants; may be NULL
+ */
+size_t flce_backward_chunked_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt,
+                                             int64_t chunk_tokens);
+flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* target,
+                                  const float* lse, const float* grad_loss, int64_t N, int64_t H,
+                                  int64_t V, flce_dtype dt, flce_reduction reduction,
+                                  int64_t chunk_tokens, void* grad_x, void* grad_W, void* ws,
+                                  size_t ws_bytes, void* hip_stream, flce_timing* timing);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,11 @@ def load() -> ctypes.CDLL:
     lib.flce_forward_timed.restype = ctypes.c_int
     lib.flce_backward_timed.argtypes = lib.flce_backward.argtypes + [tp]
     lib.flce_backward_timed.restype = ctypes.c_int
+    lib.flce_backward_chunked_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, i64]
+    lib.flce_backward_chunked_workspace_bytes.restype = sz
+    lib.flce_backward_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
+                                          vp, vp, vp, sz, vp, tp]
+    lib.flce_backward_chunked.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -176,6 +181,36 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor, lse: t
             grad_loss.data_ptr(), N, H, V, dt, _RED[reduction], gx.data_ptr(),
             gW.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device))
     code = lib.flce_backward(*args) if timer is None else lib.flce_backward_timed(*args, ctypes.byref(timer.t))
+    if code != 0:
+        raise FLCEError(code)
+    return gx, gW
+
+
+def backward_chunked_workspace_bytes(N: int, H: int, V: int, dtype: torch.dtype, chunk_tokens: int) -> int:
+    return int(load().flce_backward_chunked_workspace_bytes(N, H, V, _DT[dtype], chunk_tokens))
+
+
+def flce_backward_chunked(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor, lse: torch.Tensor,
+                          grad_loss: torch.Tensor, reduction: str = "mean", chunk_tokens: int = 1024,
+                          workspace: torch.Tensor | None = None, timer: KernelTimer | None = None):
+    """Token-chunked backward (each chunk's dlogits over the whole vocabulary), for
+    comparison with flce_backward.  Return (grad_x [N,H], grad_W [V,H])."""
+    _check(x, W, target, reduction)
+    if lse.dtype != torch.float32 or lse.shape != (x.shape[0],) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [N] tensor")
+    grad_loss = grad_loss.reshape(1).to(device=x.device, dtype=torch.float32).contiguous()
+    lib = load()
+    N, H = x.shape
+    V = W.shape[0]
+    dt = _DT[x.dtype]
+    gx = torch.empty_like(x)
+    gW = torch.empty_like(W)
+    nws = lib.flce_backward_chunked_workspace_bytes(N, H, V, dt, chunk_tokens)
+    ws = workspace if workspace is not None else torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    code = lib.flce_backward_chunked(x.data_ptr(), W.data_ptr(), target.data_ptr(), lse.data_ptr(),
+                                     grad_loss.data_ptr(), N, H, V, dt, _RED[reduction], chunk_tokens,
+                                     gx.data_ptr(), gW.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device),
+                                     ctypes.byref(timer.t) if timer is not None else None)
     if code != 0:
         raise FLCEError(code)
     return gx, gW

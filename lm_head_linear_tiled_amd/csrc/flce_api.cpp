@@ -26,7 +26,7 @@ constexpr int kFwdTargetWorkgroups = FLCE_FWD_TARGET_WGS;  // forward workgroups
 #define FLCE_PANEL_MB 128
 #endif
 constexpr size_t kDefaultPanelBytes = size_t(FLCE_PANEL_MB) << 20;  // dlogit panel budget
-constexpr int kMinVocabPerPanel = 2048;
+constexpr int kPlanCUs = 256;  // compute units the panel shape is planned for (MI355X)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -58,21 +58,66 @@ FwdPlan plan_forward(int64_t N, int64_t V) {
   return p;
 }
 
+BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb);
+
+// Estimated backward time for chunks of Nc tokens and panels of Vb vocabulary
+// entries, in units of one 256 x 256 x 256 tile contraction on one CU (a
+// persistent launch of T tiles takes ceil(T / cus) rounds of tiles, each as
+// many units as its K extent has 256-slices), plus a fixed cost per launch and
+// the float32 accumulator traffic of gradients summed over several launches.
+double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, int cus) {
+  constexpr double kLaunch = 1.0;       // launch, fill and drain
+  constexpr double kUnitsPerGB = 32.0;  // accumulator read-modify-write at ~4 TB/s
+  const int64_t th = ceil_div(H, kTile);  // hidden tiles of grad_x / grad_W, and 256-slices of H
+  auto rounds = [&](int64_t tiles) { return (double)ceil_div(tiles, cus); };
+  // chunk and panel sizes: full ones and the ragged last one
+  const int64_t nc_full = N / Nc, nc_last = N % Nc, nv_full = V / Vb, nv_last = V % Vb;
+  const int64_t n_chunks = nc_full + (nc_last ? 1 : 0), n_panels = nv_full + (nv_last ? 1 : 0);
+  double t = 0;
+  for (int ci = 0; ci < 2; ++ci) {
+    const int64_t cnt_c = ci == 0 ? nc_full : (nc_last ? 1 : 0), Kc = ci == 0 ? Nc : nc_last;
+    if (cnt_c == 0) continue;
+    for (int vi = 0; vi < 2; ++vi) {
+      const int64_t cnt_v = vi == 0 ? nv_full : (nv_last ? 1 : 0), Kv = vi == 0 ? Vb : nv_last;
+      if (cnt_v == 0) continue;
+      const int64_t tm = ceil_div(Kc, kTile), tv = ceil_div(Kv, kTile);
+      const double one = rounds(tm * tv) * th + rounds(tv * th) * tm + rounds(tm * th) * tv + 3 * kLaunch;
+      t += (double)(cnt_c * cnt_v) * one;
+    }
+  }
+  // grad_x rows are read and written once per panel after the first, grad_W rows
+  // once per chunk after the first (float32), whatever the output type
+  const double acc_gb = ((double)(n_panels - 1) * N * H + (double)(n_chunks - 1) * V * H) * 2 * 4 / 1e9;
+  return t + acc_gb * kUnitsPerGB;
+}
+
 // Dlogit panel of Nc tokens x Vb vocabulary entries holding at most panel_elems
-// values; accumulators only where a gradient is summed over several launches.
+// values: of the chunk sizes Nc (each with the widest panel that fits), the one
+// of least estimated time; accumulators only where a gradient is summed over
+// several launches.  (Also trying narrower panels that fill whole rounds of the
+// compute units was measured no better.)
 BwdPlan plan_backward_for(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t panel_elems) {
-  BwdPlan p{};
   const int64_t Np = ceil_div(N, kTile) * kTile;
   const int64_t Vp = ceil_div(V, kTile) * kTile;
-  int64_t Nc;
-  if (Np * std::min<int64_t>(Vp, kMinVocabPerPanel) <= panel_elems) {
-    Nc = Np;
-  } else {
-    Nc = std::max<int64_t>(kTile, (int64_t)std::sqrt((double)panel_elems) / kTile * kTile);
-    Nc = std::min(Nc, Np);
+  int64_t best_nc = kTile, best_vb = kTile;
+  double best = -1;
+  for (int64_t Nc = kTile; Nc <= Np; Nc += kTile) {
+    const int64_t Vb = std::min(Vp, panel_elems / Nc / kTile * kTile);
+    if (Vb < kTile) break;
+    const double c = backward_cost(N, H, V, Nc, Vb, kPlanCUs);
+    if (best < 0 || c <= best) {  // ties: the larger token chunk
+      best = c;
+      best_nc = Nc;
+      best_vb = Vb;
+    }
   }
-  int64_t Vb = std::max<int64_t>(kTile, panel_elems / Nc / kTile * kTile);
-  Vb = std::min(Vb, Vp);
+  return plan_backward_shape(N, H, V, dt, best_nc, best_vb);
+}
+
+// Plan for chunks of Nc tokens and panels of Vb vocabulary entries (both
+// multiples of kTile, at most the padded N and V).
+BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb) {
+  BwdPlan p{};
   p.Nc = (int)Nc;
   p.Ncp = (int)Nc;  // a multiple of kTile
   p.n_chunks = (int)ceil_div(N, Nc);
@@ -107,6 +152,14 @@ bool plan_backward(int64_t N, int64_t H, int64_t V, flce_dtype dt, size_t ws_byt
     if (elems <= min_elems) return false;
     elems = std::max(min_elems, elems / 2);
   }
+}
+
+// Token chunks of chunk_tokens (rounded up to kTile, at most the padded N), each
+// with the whole vocabulary as one panel.
+BwdPlan plan_backward_chunked(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t chunk_tokens) {
+  const int64_t Np = ceil_div(N, kTile) * kTile;
+  const int64_t Nc = std::min(Np, ceil_div(chunk_tokens, kTile) * kTile);
+  return plan_backward_shape(N, H, V, dt, Nc, ceil_div(V, kTile) * kTile);
 }
 
 struct Range {
@@ -246,6 +299,41 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   if (any_alias(in, 5, out, 2, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
   BwdPlan p;
   if (!ws || !plan_backward(N, H, V, dt, ws_bytes, &p)) return FLCE_ERR_WORKSPACE;
+  p.max_workgroups = flce::device_cu_count();
+
+  char* base = (char*)ws;
+  const float red_scale = reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f;
+  flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  rec.start();
+  hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
+                                       grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
+                                       (float*)(base + p.off_gw), (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+size_t flce_backward_chunked_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t chunk_tokens) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || chunk_tokens < 1) return 0;
+  return plan_backward_chunked(N, H, V, dt, chunk_tokens).total;
+}
+
+flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* target, const float* lse,
+                                  const float* grad_loss, int64_t N, int64_t H, int64_t V, flce_dtype dt,
+                                  flce_reduction reduction, int64_t chunk_tokens, void* grad_x, void* grad_W,
+                                  void* ws, size_t ws_bytes, void* hip_stream, flce_timing* timing) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (chunk_tokens < 1) return FLCE_ERR_SHAPE;
+  if (!lse || !grad_loss || !grad_x || !grad_W) return FLCE_ERR_NULL;
+  const size_t es = esize(dt);
+  const Range in[5] = {{x, (size_t)N * H * es},
+                       {W, (size_t)V * H * es},
+                       {target, 8 * (size_t)N},
+                       {lse, 4 * (size_t)N},
+                       {grad_loss, 4}};
+  const Range out[2] = {{grad_x, (size_t)N * H * es}, {grad_W, (size_t)V * H * es}};
+  if (any_alias(in, 5, out, 2, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
+  BwdPlan p = plan_backward_chunked(N, H, V, dt, chunk_tokens);
+  if (!ws || ws_bytes < p.total) return FLCE_ERR_WORKSPACE;
   p.max_workgroups = flce::device_cu_count();
 
   char* base = (char*)ws;

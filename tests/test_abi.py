@@ -134,3 +134,40 @@ def test_forward_backward_rejects(lib):
     n = lib.flce_forward_backward_workspace_bytes(64, 128, 1000, F32)
     assert n >= 256 + lib.flce_forward_workspace_bytes(64, 128, 1000, F32)
     assert n >= 256 + lib.flce_backward_workspace_bytes(64, 128, 1000, F32)
+
+
+def bch(lib, x=X, W=Wp, t=T, lse=LSE, gl=GL, N=64, H=128, V=1000, dt=F32, red=MEAN, chunk=256, gx=GX, gw=GW,
+        ws=WSP, nws=None):
+    if nws is None:
+        nws = lib.flce_backward_chunked_workspace_bytes(N, H, V, dt, chunk) if min(N, H, V, chunk) > 0 else 0
+    return lib.flce_backward_chunked(x, W, t, lse, gl, N, H, V, dt, red, chunk, gx, gw, ws, nws, None, None)
+
+
+def test_backward_chunked_workspace_sizes(lib):
+    # one chunk of every token over the whole vocabulary; many chunks need the
+    # float32 grad_W accumulator for bfloat16 only
+    N, H, V = 4096, 4096, 128256
+    one = lib.flce_backward_chunked_workspace_bytes(N, H, V, BF16, N)
+    assert one >= 2 * N * ((V + 255) // 256 * 256)
+    many = lib.flce_backward_chunked_workspace_bytes(N, H, V, BF16, 256)
+    assert many >= 2 * 256 * V + 4 * V * H
+    assert lib.flce_backward_chunked_workspace_bytes(N, H, V, F32, 256) < 4 * V * H
+    assert lib.flce_backward_chunked_workspace_bytes(N, H, V, BF16, 10 ** 9) == one  # capped at N
+    assert lib.flce_backward_chunked_workspace_bytes(N, H, V, BF16, 1) == many       # rounded up to 256
+    assert lib.flce_backward_chunked_workspace_bytes(N, H, V, BF16, 0) == 0
+    assert lib.flce_backward_chunked_workspace_bytes(0, H, V, BF16, 256) == 0
+
+
+def test_backward_chunked_rejects(lib):
+    assert bch(lib, chunk=0) == SHAPE
+    assert bch(lib, chunk=-5) == SHAPE
+    assert bch(lib, lse=None) == NULL
+    assert bch(lib, gw=None) == NULL
+    assert bch(lib, N=0) == SHAPE
+    assert bch(lib, dt=3) == DTYPE
+    assert bch(lib, red=7) == RED
+    assert bch(lib, W=Wp + 4) == ALIGN
+    assert bch(lib, gx=T) == ALIAS
+    assert bch(lib, ws=GX + 16) == ALIAS
+    assert bch(lib, ws=None) == WS
+    assert bch(lib, nws=lib.flce_backward_chunked_workspace_bytes(64, 128, 1000, F32, 256) - 1) == WS
