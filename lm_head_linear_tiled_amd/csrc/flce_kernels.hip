@@ -249,13 +249,20 @@ __global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block
 // t = lid, lid + G, ... of its launch (lid: XCD-grouped id, G: grid size), each
 // tile (tm, tn) taken in the grouped order, so the copy of a tile's first K slice
 // overlaps the previous tile's last slice and epilogue.
+template <int GM = FLCE_GROUP_M>
 __device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int G = (int)gridDim.x;
   const int t = xcd_grouped_id((int)blockIdx.x, G) + j * G;
   if (t >= tiles_m * tiles_n) return false;
-  grouped_tile(t, tiles_m, tiles_n, tm, tn);
+  grouped_tile<GM>(t, tiles_m, tiles_n, tm, tn);
   return true;
 }
+
+// Tile groups of the dlogit and grad_x launches: 8 rows (vocabulary tiles of W,
+// hidden tiles of W) per group, measured better there than 4.
+#ifndef FLCE_GROUP_M_WIDE
+#define FLCE_GROUP_M_WIDE 8
+#endif
 
 // Four consecutive float outputs as 4 elements of T (bfloat16: hardware
 // round-to-nearest-even conversion), and the 16-byte LDS accesses of the
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   const float s = grad_loss[0] * red_scale;
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_v, tiles_t, tm, tn)) return false;
+    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_v, tiles_t, tm, tn)) return false;
     m0 = v0 + tm * kTile;
     n0 = i0 + tn * kTile;
     return true;
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   const Operand<T> B{panel, Vbp, Kc, Vbp};
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_h, tiles_t, tm, tn)) return false;
+    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_h, tiles_t, tm, tn)) return false;
     m0 = tm * kTile;
     n0 = tn * kTile;
     return true;

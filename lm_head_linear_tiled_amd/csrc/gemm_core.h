@@ -484,8 +484,8 @@ __device__ __forceinline__ int xcd_grouped_id(int b, int G) {
 // GM tile rows column by column: any GM * c consecutive ids form a GM x c block,
 // so the 32 workgroups an XCD runs at once share GM row tiles and 32 / GM column
 // tiles of the operands in its L2 (GM = 1: plain row-fastest order).
+template <int GM = FLCE_GROUP_M>
 __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = FLCE_GROUP_M;
   if (GM <= 1) {
     tm = t % tiles_m;
     tn = t / tiles_m;
