@@ -100,9 +100,11 @@ flce_status flce_forward(const void* x, const void* W, const int64_t* target, in
                          size_t ws_bytes, void* hip_stream);
 
 /* Bytes of device workspace flce_backward needs for these sizes (a pure function
- * of its arguments; 0 for invalid arguments).  A larger workspace lets the
- * backward use larger dlogit panels (fewer passes); a smaller one, down to
- * flce_backward_min_workspace_bytes, makes it use smaller panels. */
+ * of its arguments; 0 for invalid arguments): the dlogit panel of its default
+ * plan (at most 128 MB, its shape chosen for these sizes) plus float32
+ * accumulators where a gradient is summed over several panels or token chunks.
+ * A smaller workspace, down to flce_backward_min_workspace_bytes, makes the
+ * backward use smaller panels (more passes); a larger one changes nothing. */
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
 size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
 

@@ -15,11 +15,14 @@
 //   fwd_loss      sums the block partials in a fixed order into the scalar loss.
 // Backward (helion PR #1268: the backward recomputes the logits; the dlogits
 // drive both gradients; Liger-Kernel PR #928: zero the out-of-range dlogits):
-//   bwd_dlogits   recomputes a logit tile S = x_tile . W_tile^T and writes
-//                 D = s (exp(S - lse) - onehot) into a bounded panel, exactly 0
-//                 outside i < N, v < V;
+//   bwd_dlogits   recomputes a logit tile S^T = W_tile . x_tile^T and writes
+//                 D = s (exp(S - lse) - onehot) into a bounded panel [token][vocab],
+//                 exactly 0 outside i < N, v < V;
 //   bwd_grad_w    grad_W[v, h] (+)= sum_i D[i, v] x[i, h] over the panel's tokens;
 //   bwd_grad_x    grad_x[i, h] (+)= sum_v D[i, v] W[v, h] over the panel's vocabulary.
+// The three backward kernels compute transposed tiles (the output's contiguous
+// dimension on the accumulator rows) and write them through the LDS stage their
+// last K slice frees (staged_epilogue), as whole 128-byte lines.
 #include "gemm_core.h"
 #include "flce_launch.h"
 

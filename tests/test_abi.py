@@ -171,3 +171,17 @@ def test_backward_chunked_rejects(lib):
     assert bch(lib, ws=GX + 16) == ALIAS
     assert bch(lib, ws=None) == WS
     assert bch(lib, nws=lib.flce_backward_chunked_workspace_bytes(64, 128, 1000, F32, 256) - 1) == WS
+
+
+def test_backward_plan_shapes(lib):
+    """The panel shape the backward picks, read off the workspace it asks for
+    (panel + float32 accumulators), at the headline and at N=32768, V=32000."""
+    MB = 1 << 20
+    # headline: 4096 tokens x 16384 vocabulary (128 MB bf16) + grad_x accumulator [N, H] f32
+    assert lib.flce_backward_workspace_bytes(4096, 4096, 128256, BF16) == 128 * MB + 4096 * 4096 * 4
+    # 8192 x 8192 panel (not 32768 x 2048, whose grad_W launches would fill half the CUs)
+    # + grad_x accumulator [N, H] + grad_W accumulator [8192, H]
+    assert lib.flce_backward_workspace_bytes(32768, 4096, 32000, BF16) == \
+        128 * MB + 32768 * 4096 * 4 + 8192 * 4096 * 4
+    # a single panel covers a small problem: no accumulators
+    assert lib.flce_backward_workspace_bytes(2048, 4096, 32000, BF16) == 2048 * 32000 * 2
