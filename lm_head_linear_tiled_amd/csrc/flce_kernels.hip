@@ -343,20 +343,6 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
   }
 }
 
-// 16 bytes holding four floats, added to the four floats at p; returns the sums.
-__device__ __forceinline__ float4 add4(uint4 v, const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  return make_float4(__uint_as_float(v.x) + a.x, __uint_as_float(v.y) + a.y, __uint_as_float(v.z) + a.z,
-                     __uint_as_float(v.w) + a.w);
-}
-__device__ __forceinline__ float4 as_float4(uint4 v) {
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-}
-// Four floats stored as T at p (bfloat16: round to nearest even).
-__device__ __forceinline__ void store_out4(bf16_t* p, float4 f) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
-}
-__device__ __forceinline__ void store_out4(float* p, float4 f) { *reinterpret_cast<float4*>(p) = f; }
 
 // Sᵀ tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major), as
 // in the forward, so lse and target are read once per token column; the D tile
@@ -420,21 +406,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   G::run_tiles(A, B, H, lds, acc, next, store);
 }
 
-// Final or accumulated output of a backward contraction through the staged
-// epilogue: out rows are the N side of the tile (row_ok tells which exist and
-// row_off gives their element offset), M (hidden) is contiguous.
-//   accumulate: add the float32 partial sums in acc_buf first
-//   final:      write T to dst, else float32 to acc_buf
-// A tile that is neither accumulated nor kept in float32 stages T directly.
+// Output of a backward contraction through the staged epilogue: out rows are
+// the N side of the tile (row_ok tells which exist and row_off gives their
+// element offset), M (hidden) is contiguous.  final: write T to dst, else the
+// float32 partial sums to acc_buf (the sums of earlier launches are already in
+// acc, see grad_init); a final tile stages T directly.
 template <typename T, class G, class RowOk, class RowOff>
-__device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare, int hw, int nw, int H,
-                                              int accumulate, int final, T* __restrict__ dst,
-                                              float* __restrict__ acc_buf, RowOk&& row_ok, RowOff&& row_off) {
+__device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare, int hw, int nw, int H, int final,
+                                              T* __restrict__ dst, float* __restrict__ acc_buf, RowOk&& row_ok,
+                                              RowOff&& row_off) {
   auto val = [&](int i, int j, int g, float* d) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) d[u] = acc[i][j][4 * g + u];
   };
-  if (!accumulate && final) {
+  if (final) {
     staged_epilogue<T, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
       if (!row_ok(nw + n) || hw + m >= H) return;
       *reinterpret_cast<uint4*>(dst + row_off(nw + n) + hw + m) = v;
@@ -442,13 +427,41 @@ __device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare,
   } else {
     staged_epilogue<float, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
       if (!row_ok(nw + n) || hw + m >= H) return;
-      const int64_t o = row_off(nw + n) + hw + m;
-      const float4 f = accumulate ? add4(v, acc_buf + o) : as_float4(v);
-      if (final)
-        store_out4(dst + o, f);
-      else
-        *reinterpret_cast<float4*>(acc_buf + o) = f;
+      *reinterpret_cast<uint4*>(acc_buf + row_off(nw + n) + hw + m) = v;
     });
+  }
+}
+
+// Start of a gradient tile: zero, or, when the output is summed over several
+// launches, the float32 partial sums so far, loaded straight into the
+// accumulator layout (four consecutive hidden entries of one output row per lane
+// and group, 16 bytes) while the tile's first K slice is copied; the epilogue
+// then only stores.
+template <class G, class RowOk, class RowOff>
+__device__ __forceinline__ void grad_init(typename G::Acc& acc, int hw, int nw, int H, int accumulate,
+                                          const float* __restrict__ acc_buf, RowOk&& row_ok, RowOff&& row_off) {
+  if (!accumulate) {
+    G::zero(acc);
+    return;
+  }
+  const int l = (int)threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < G::FN; ++j) {
+    const int n = nw + j * 32 + (l & 31);
+    const bool ok = row_ok(n);
+    const int64_t base = ok ? row_off(n) : 0;
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int h = hw + i * 32 + 8 * g + 4 * (l >> 5);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok && h < H) v = *reinterpret_cast<const float4*>(acc_buf + base + h);
+        acc[i][j][4 * g + 0] = v.x;
+        acc[i][j][4 * g + 1] = v.y;
+        acc[i][j][4 * g + 2] = v.z;
+        acc[i][j][4 * g + 3] = v.w;
+      }
   }
 }
 
@@ -474,13 +487,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
     n0 = tn * kTile;
     return true;
   };
+  auto row_ok = [&](int v) { return v < Vb && v0 + v < V; };
+  auto row_off = [&](int v) { return (int64_t)v * H; };
+  auto init = [&](typename G::Acc& acc, int m0, int n0) {
+    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, gw_acc, row_ok, row_off);
+  };
   auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    grad_epilogue<T, G>(
-        acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, final, gw_out, gw_acc,
-        [&](int v) { return v < Vb && v0 + v < V; }, [&](int v) { return (int64_t)v * H; });
+    grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gw_out, gw_acc, row_ok, row_off);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Kc, lds, acc, next, store);
+  G::run_tiles(A, B, Kc, lds, acc, next, store, init);
 }
 
 // grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
@@ -504,13 +520,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
     n0 = tn * kTile;
     return true;
   };
+  auto row_ok = [&](int t) { return t < Kc && i0 + t < N; };
+  auto row_off = [&](int t) { return (int64_t)(i0 + t) * H; };
+  auto init = [&](typename G::Acc& acc, int m0, int n0) {
+    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, gx_acc, row_ok, row_off);
+  };
   auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    grad_epilogue<T, G>(
-        acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, final, gx_out, gx_acc,
-        [&](int t) { return t < Kc && i0 + t < N; }, [&](int t) { return (int64_t)(i0 + t) * H; });
+    grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gx_out, gx_acc, row_ok, row_off);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Kv, lds, acc, next, store);
+  G::run_tiles(A, B, Kv, lds, acc, next, store, init);
 }
 
 __global__ void fill_scalar(float* p, float v) { p[0] = v; }

@@ -408,18 +408,20 @@ struct TileGemm {
 
   // Persistent main loop over a sequence of output tiles with K = K each:
   // next(j, m0, n0) gives the origin of the j-th tile (false past the last one) and
-  // epi(acc, m0, n0, spare) consumes a finished tile, after which acc restarts at
-  // zero.  The slices of all tiles form one stream through two LDS stages, so the
-  // first slice of tile j + 1 is copied while the last slice of tile j is
-  // multiplied and its epilogue runs.  spare is the stage that last slice was
+  // epi(acc, m0, n0, spare) consumes a finished tile; init(acc, m0, n0) (zero by
+  // default) sets acc up before a tile's first slice, after that slice's copies
+  // are issued, so loads it issues are covered by the barrier's vmcnt wait.  The
+  // slices of all tiles form one stream through two LDS stages, so the first
+  // slice of tile j + 1 is copied while the last slice of tile j is multiplied
+  // and its epilogue runs.  spare is the stage that last slice was
   // read from: an epilogue may use its STAGE_BYTES after a workgroup barrier
   // (other waves may still be reading their last fragments from it) and until
   // it returns (the next slice's copies into it start after the barrier that
   // opens that slice).  Every wave of the workgroup calls epi for the same tiles.
   // Ends with a barrier: the caller may reuse the LDS afterwards.
-  template <class Next, class Epi>
+  template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
-                                                   Next&& next, Epi&& epi) {
+                                                   Next&& next, Epi&& epi, Init&& init) {
     static_assert(NSTAGE == 2, "the persistent loop double-buffers K slices");
     constexpr int AOFF = A_BYTES / ES;
     const int KT = (K + BK - 1) / BK;
@@ -439,7 +441,7 @@ struct TileGemm {
       }
     };
     advance();
-    zero(acc);
+    init(acc, tm0, tn0);
     int q = 0;
     for (int j = 0;;) {
       for (int kt = 0; kt < KT; ++kt, ++q) {
@@ -449,9 +451,15 @@ struct TileGemm {
       }
       epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
       if (!next(++j, tm0, tn0)) break;
-      zero(acc);
+      init(acc, tm0, tn0);
     }
     wait_and_barrier<0>();
+  }
+
+  template <class Next, class Epi>
+  static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
+                                                   Next&& next, Epi&& epi) {
+    run_tiles(A, B, K, lds, acc, next, epi, [](Acc& a, int, int) { zero(a); });
   }
 
   // acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T for a single tile.
