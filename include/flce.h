@@ -165,7 +165,8 @@ typedef enum {
   FLCE_K_BWD_DLOGITS = 3, /* logit tile recompute -> dlogit panel                   */
   FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
   FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel              */
-  FLCE_K_FILL = 6         /* writes the implicit grad_loss of 1                    */
+  FLCE_K_FILL = 6,        /* writes the implicit grad_loss of 1                    */
+  FLCE_K_BWD_GX_REDUCE = 7 /* adds the K-split partial sums of a grad_x launch       */
 } flce_kernel;
 
 typedef struct {

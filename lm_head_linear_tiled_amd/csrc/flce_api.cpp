@@ -60,6 +60,16 @@ FwdPlan plan_forward(int64_t N, int64_t V) {
 
 BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb);
 
+// grad_x K splits for chunks of Nc tokens and panels of Vb entries: when a
+// grad_x launch has fewer output tiles than half the compute units, its K
+// (vocabulary) range is split over up to 4 workgroups per tile, each keeping at
+// least 2048 entries; the float32 partial sums are added by a small kernel.
+int64_t gx_splits_for(int64_t Nc, int64_t Vb, int64_t H) {
+  const int64_t tiles = ceil_div(Nc, kTile) * ceil_div(H, kTile);
+  const int64_t ks = std::min<int64_t>({4, kPlanCUs / tiles, Vb / 2048});
+  return ks >= 2 ? ks : 1;
+}
+
 // Estimated backward time for chunks of Nc tokens and panels of Vb vocabulary
 // entries, in units of one 256 x 256 x 256 tile contraction on one CU (a
 // persistent launch of T tiles takes ceil(T / cus) rounds of tiles, each as
@@ -81,7 +91,9 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
       const int64_t cnt_v = vi == 0 ? nv_full : (nv_last ? 1 : 0), Kv = vi == 0 ? Vb : nv_last;
       if (cnt_v == 0) continue;
       const int64_t tm = ceil_div(Kc, kTile), tv = ceil_div(Kv, kTile);
-      const double one = rounds(tm * tv) * th + rounds(tv * th) * tm + rounds(tm * th) * tv + 3 * kLaunch;
+      const int64_t ks = gx_splits_for(Nc, Vb, H);
+      double one = rounds(tm * tv) * th + rounds(tv * th) * tm + rounds(tm * th * ks) * ceil_div(tv, ks) + 3 * kLaunch;
+      if (ks > 1) one += kLaunch + (double)(ks + 1) * Kc * H * 4 / 1e9 * kUnitsPerGB;  // partial-sum pass
       t += (double)(cnt_c * cnt_v) * one;
     }
   }
@@ -128,6 +140,8 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   // float32 gradients accumulate in place; bfloat16 ones through float32 buffers.
   p.gx_bytes = (dt == FLCE_BF16 && p.n_panels > 1) ? sizeof(float) * (size_t)N * H : 0;
   p.gw_bytes = (dt == FLCE_BF16 && p.n_chunks > 1) ? sizeof(float) * (size_t)Vb * H : 0;
+  p.gx_splits = (int)gx_splits_for(Nc, Vb, H);
+  p.gxpart_bytes = p.gx_splits > 1 ? sizeof(float) * (size_t)p.gx_splits * p.Ncp * H : 0;
   size_t o = 0;
   p.off_panel = o;
   o = align_up(o + es * (size_t)p.Ncp * p.Vbp, 256);
@@ -135,6 +149,8 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   o = align_up(o + p.gx_bytes, 256);
   p.off_gw = o;
   o = align_up(o + p.gw_bytes, 256);
+  p.off_gxpart = o;
+  o = align_up(o + p.gxpart_bytes, 256);
   p.total = o;
   return p;
 }
@@ -307,7 +323,8 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   rec.start();
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
-                                       (float*)(base + p.off_gw), (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
+                                       (hipStream_t)hip_stream, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -342,7 +359,8 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
   rec.start();
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
-                                       (float*)(base + p.off_gw), (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
+                                       (hipStream_t)hip_stream, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -388,7 +406,7 @@ flce_status flce_forward_backward(const void* x, const void* W, const int64_t* t
     e = flce::launch_backward((int)dt, bp, x, W, target, lse, gl,
                               reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f, (int)N, (int)H, (int)V,
                               grad_x, grad_W, base + bp.off_panel, (float*)(base + bp.off_gx),
-                              (float*)(base + bp.off_gw), s, rec);
+                              (float*)(base + bp.off_gw), (float*)(base + bp.off_gxpart), s, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

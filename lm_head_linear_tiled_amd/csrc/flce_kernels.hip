@@ -501,35 +501,90 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
 
 // grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
 // vocabulary][m = hidden], MN-major), cols = chunk tokens (B = the panel as [n =
-// token][k = vocabulary], K-major); written as grad_x rows i0 + n.
+// token][k = vocabulary], K-major); written as grad_x rows i0 + n.  With ks > 1
+// the panel's vocabulary is split into ks ranges of Ks entries: work item
+// (split s, tile) covers range s and writes its float32 partial sums to
+// part + s * Ncp * H (rows chunk-local); split 0 starts from the sums of earlier
+// panels; bwd_gx_reduce adds the splits.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
                                                        const T* __restrict__ W, int H, int N, int i0, int v0,
-                                                       int tiles_h, int tiles_t, T* __restrict__ gx_out,
-                                                       float* __restrict__ gx_acc, int accumulate, int final) {
+                                                       int tiles_h, int tiles_t, int ks, int Ks, int Ncp,
+                                                       T* __restrict__ gx_out, float* __restrict__ gx_acc,
+                                                       float* __restrict__ part, int accumulate, int final) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int wm = G::wave_m(), wn = G::wave_n();
   const Operand<T> A{W + (int64_t)v0 * H, H, H, Kv};
   const Operand<T> B{panel, Vbp, Kc, Vbp};
-  auto next = [&](int j, int& m0, int& n0) {
+  const int tiles = tiles_h * tiles_t;
+  // the j-th work item of this workgroup: split s, tile origin (m0, n0)
+  auto item = [&](int j, int& s, int& m0, int& n0) {
+    const int G_ = (int)gridDim.x;
+    const int t = xcd_grouped_id((int)blockIdx.x, G_) + j * G_;
+    if (t >= tiles * ks) return false;
+    s = t / tiles;
     int tm, tn;
-    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_h, tiles_t, tm, tn)) return false;
+    grouped_tile<FLCE_GROUP_M_WIDE>(t - s * tiles, tiles_h, tiles_t, tm, tn);
     m0 = tm * kTile;
     n0 = tn * kTile;
     return true;
   };
+  auto next = [&](int j, int& m0, int& n0, int& kb) {
+    int s;
+    if (!item(j, s, m0, n0)) return false;
+    kb = s * Ks;
+    return true;
+  };
   auto row_ok = [&](int t) { return t < Kc && i0 + t < N; };
   auto row_off = [&](int t) { return (int64_t)(i0 + t) * H; };
+  auto row_local = [&](int t) { return (int64_t)t * H; };
+  int ji = 0, je = 0;  // items started / finished by this workgroup
   auto init = [&](typename G::Acc& acc, int m0, int n0) {
-    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, gx_acc, row_ok, row_off);
+    int s, a0, a1;
+    item(ji++, s, a0, a1);
+    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate && s == 0, gx_acc, row_ok, row_off);
   };
   auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gx_out, gx_acc, row_ok, row_off);
+    int s, a0, a1;
+    item(je++, s, a0, a1);
+    if (ks == 1)
+      grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gx_out, gx_acc, row_ok, row_off);
+    else
+      grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, 0, gx_out,
+                          part + (int64_t)s * Ncp * H, row_ok, row_local);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Kv, lds, acc, next, store, init);
+  G::run_tiles(A, B, Ks, lds, acc, next, store, init);
+}
+
+// Sum of the ks float32 partial grad_x row blocks [Kc, H] (fixed order) into
+// grad_x rows i0.. (final: as T) or into their float32 accumulator.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gx_reduce(const float* __restrict__ part, int ks, int64_t stride, int Kc,
+                                                     int H, int i0, int final, T* __restrict__ gx_out,
+                                                     float* __restrict__ gx_acc) {
+  const int64_t n4 = (int64_t)Kc * H / 4;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (int64_t)gridDim.x * 256) {
+    float4 a = reinterpret_cast<const float4*>(part)[q];
+    for (int s = 1; s < ks; ++s) {
+      const float4 b = reinterpret_cast<const float4*>(part + s * stride)[q];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const int64_t o = (int64_t)i0 * H + 4 * q;
+    if (final) {
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint2*>(gx_out + o) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+      else
+        *reinterpret_cast<float4*>(gx_out + o) = a;
+    } else {
+      *reinterpret_cast<float4*>(gx_acc + o) = a;
+    }
+  }
 }
 
 __global__ void fill_scalar(float* p, float v) { p[0] = v; }
@@ -575,8 +630,8 @@ hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W
 template <typename T>
 static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv, const int64_t* target,
                                const float* lse, const float* grad_loss, float red_scale, int N, int H, int V,
-                               void* gxv, void* gwv, void* panelv, float* gx_acc, float* gw_acc, hipStream_t st,
-                               Recorder& rec) {
+                               void* gxv, void* gwv, void* panelv, float* gx_acc, float* gw_acc, float* gx_part,
+                               hipStream_t st, Recorder& rec) {
   const T* x = (const T*)xv;
   const T* W = (const T*)Wv;
   T* gx = (T*)gxv;
@@ -607,10 +662,22 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
                          V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
                          c == p.n_chunks - 1 ? 1 : 0);
       rec.after(FLCE_K_BWD_GRAD_W);
-      // grad_x rows of this chunk accumulate over vocabulary panels.
-      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, Kv, W,
-                         H, N, i0, v0, tiles_h, tiles_m, gx, gxa, pv > 0 ? 1 : 0, pv == p.n_panels - 1 ? 1 : 0);
+      // grad_x rows of this chunk accumulate over vocabulary panels; a launch with
+      // few output tiles splits the panel's vocabulary (partial sums in gx_part).
+      constexpr int BK = Cfg<T>::BK;
+      const int Ks = (int)((((int64_t)Kv + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
+      const int ks = (Kv + Ks - 1) / Ks;
+      const int acc_x = pv > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
+      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc,
+                         Kv, W, H, N, i0, v0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x);
       rec.after(FLCE_K_BWD_GRAD_X);
+      if (ks > 1) {
+        const int64_t n4 = (int64_t)Kc * H / 4;
+        const int rgrid = (int)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)p.max_workgroups);
+        hipLaunchKernelGGL(bwd_gx_reduce<T>, dim3(rgrid), dim3(256), 0, st, (const float*)gx_part, ks,
+                           (int64_t)p.Ncp * H, Kc, H, i0, fin_x, gx, gxa);
+        rec.after(FLCE_K_BWD_GX_REDUCE);
+      }
     }
   }
   const hipError_t e = hipGetLastError();
@@ -619,12 +686,12 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
-                           void* gw, void* panel, float* gx_acc, float* gw_acc, hipStream_t st,
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, hipStream_t st,
                            Recorder& rec) {
   return dt == 1 ? launch_bwd_t<bf16_t>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                        gw_acc, st, rec)
+                                        gw_acc, gx_part, st, rec)
                  : launch_bwd_t<float>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                       gw_acc, st, rec);
+                                       gw_acc, gx_part, st, rec);
 }
 
 }  // namespace flce

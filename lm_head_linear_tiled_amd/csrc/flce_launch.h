@@ -24,8 +24,9 @@ struct BwdPlan {
   int Nc, n_chunks;         // tokens per chunk, chunks
   int Vb, Vbp, n_panels;    // vocabulary per panel, padded, panels
   int Ncp;                  // Nc padded to kTile
-  size_t off_panel, off_gx, off_gw, total;  // workspace carving (bytes); 0-sized parts unused
-  size_t gx_bytes, gw_bytes;
+  int gx_splits;            // grad_x K splits per launch (1: none), partial sums in gxpart
+  size_t off_panel, off_gx, off_gw, off_gxpart, total;  // workspace carving (bytes); 0-sized parts unused
+  size_t gx_bytes, gw_bytes, gxpart_bytes;
   int max_workgroups;                       // persistent grid size: one workgroup per CU
 };
 
@@ -69,7 +70,7 @@ hipError_t launch_fill(float* p, float v, hipStream_t st, Recorder& rec);
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
-                           void* gw, void* panel, float* gx_acc, float* gw_acc, hipStream_t st,
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, hipStream_t st,
                            Recorder& rec);
 
 }  // namespace flce

@@ -419,25 +419,38 @@ struct TileGemm {
   // it returns (the next slice's copies into it start after the barrier that
   // opens that slice).  Every wave of the workgroup calls epi for the same tiles.
   // Ends with a barrier: the caller may reuse the LDS afterwards.
+  // next(j, m0, n0) or next(j, m0, n0, kb): the second form also gives the K
+  // offset at which the tile's K range of length K starts (split-K tiles).
+  template <class Next>
+  static __device__ __forceinline__ bool next_tile(Next& next, int j, int& m0, int& n0, int& kb) {
+    if constexpr (std::is_invocable_v<Next&, int, int&, int&, int&>) {
+      return next(j, m0, n0, kb);
+    } else {
+      kb = 0;
+      return next(j, m0, n0);
+    }
+  }
+
   template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
                                                    Next&& next, Epi&& epi, Init&& init) {
     static_assert(NSTAGE == 2, "the persistent loop double-buffers K slices");
     constexpr int AOFF = A_BYTES / ES;
     const int KT = (K + BK - 1) / BK;
-    int tm0, tn0;
-    if (!next(0, tm0, tn0)) return;
-    // copy cursor: slice pk of tile pj, origin (pm0, pn0); past the last tile it
-    // points at a K offset beyond every operand, so its copies read zeros
-    int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0;
+    int tm0, tn0, tkb;
+    if (!next_tile(next, 0, tm0, tn0, tkb)) return;
+    // copy cursor: slice pk of tile pj, origin (pm0, pn0), K offset pkb; past the
+    // last tile it points at K offset KT * BK, and its copies (into a stage no
+    // slice reads) stay inside the operands or read zeros
+    int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0, pkb = tkb;
     bool pvalid = true;
-    load_tile<AMAJ, BM>(A, pm0, 0, lds);
-    load_tile<BMAJ, BN>(B, pn0, 0, lds + AOFF);
+    load_tile<AMAJ, BM>(A, pm0, pkb, lds);
+    load_tile<BMAJ, BN>(B, pn0, pkb, lds + AOFF);
     auto advance = [&]() {
       if (++pk == KT) {
         pk = 0;
         ++pj;
-        pvalid = pvalid && next(pj, pm0, pn0);
+        pvalid = pvalid && next_tile(next, pj, pm0, pn0, pkb);
       }
     };
     advance();
@@ -446,11 +459,11 @@ struct TileGemm {
     for (int j = 0;;) {
       for (int kt = 0; kt < KT; ++kt, ++q) {
         wait_and_barrier<0>();
-        slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pk * BK : KT * BK, acc);
+        slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pkb + pk * BK : KT * BK, acc);
         advance();
       }
       epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
-      if (!next(++j, tm0, tn0)) break;
+      if (!next_tile(next, ++j, tm0, tn0, tkb)) break;
       init(acc, tm0, tn0);
     }
     wait_and_barrier<0>();

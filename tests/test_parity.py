@@ -75,6 +75,30 @@ def test_small_workspace_panels(gpu, dtype, reduction):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_grad_x_split_k(gpu, dtype, reduction):
+    """Few grad_x output tiles (2 x 2): the panel's vocabulary is split over four
+    workgroups per tile, the last range ragged, and bwd_gx_reduce adds them."""
+    N, H, V = 512, 512, 9000
+    got = check_case(gpu, N, H, V, dtype, reduction, seed=21, grad_loss=0.9)
+    x, W, t = make_inputs(N, H, V, dtype, seed=21)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(16)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.9], device="cuda"), reduction, timer=bt)
+    torch.cuda.synchronize()
+    assert [k for k, _ in bt.durations()] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "bwd_gx_reduce"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_x_split_k_several_panels(gpu, dtype):
+    """Split grad_x launches over three vocabulary panels: the first split of each
+    tile starts from the earlier panels' partial sums."""
+    N, H, V = 512, 256, 40000
+    nws = gpu.backward_workspace_bytes(N, H, V, torch.float32 if dtype == "f32" else torch.bfloat16) // 2
+    check_case(gpu, N, H, V, dtype, "mean", seed=22, bwd_ws_bytes=nws)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_w_zero_closed_form(gpu, dtype):
     """W = 0: lse = ln V and loss = ln V (mean), grad_x = 0 exactly."""
     N, H, V = 200, 64, 777
