@@ -379,28 +379,51 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
     bool tv[G::FN];
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
+      // unconditional loads (clamped index), all in flight together
       const int tok = tw + j * 32 + (l & 31);
+      const int tc = tok < N ? tok : N - 1;
+      const int64_t t64 = target[tc];
+      const float lv = lse[tc];
       tv[j] = tok < N;
-      const int64_t t64 = tv[j] ? target[tok] : -1;
-      lr[j] = tv[j] ? lse[tok] * kLog2e : 0.f;
-      tt[j] = t64 >= 0 && t64 < V ? (int)t64 : -1;
+      lr[j] = tv[j] ? lv * kLog2e : 0.f;
+      tt[j] = tv[j] && t64 >= 0 && t64 < V ? (int)t64 : -1;
     }
-    staged_epilogue<T, G::FM, G::FN>(
-        spare,
-        [&](int i, int j, int g, float* d) {
+    auto out = [&](int n, int m, uint4 v) {
+      *reinterpret_cast<uint4*>(panel + (int64_t)(tw + n - i0) * Vbp + (vw - v0) + m) = v;
+    };
+    if (m0 + kTile <= V && n0 + kTile <= N) {
+      // interior tile: no masks; the one-hot term as -s at the target row, found
+      // from the target's row offset lt within this lane's rows of the group
+      int lt[G::FN];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
-            d[u] = 0.f;
-            if (tv[j] && v < V) {
-              const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr[j]);
-              d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
+      for (int j = 0; j < G::FN; ++j) lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
+      staged_epilogue<T, G::FM, G::FN>(
+          spare,
+          [&](int i, int j, int g, float* d) {
+            const int r = lt[j] - (i * 32 + 8 * g);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lr[j]));
+              d[u] = __builtin_fmaf(s, p, r == u ? -s : 0.f);
             }
-          }
-        },
-        [&](int n, int m, uint4 v) {
-          *reinterpret_cast<uint4*>(panel + (int64_t)(tw + n - i0) * Vbp + (vw - v0) + m) = v;
-        });
+          },
+          out);
+    } else {
+      staged_epilogue<T, G::FM, G::FN>(
+          spare,
+          [&](int i, int j, int g, float* d) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
+              d[u] = 0.f;
+              if (tv[j] && v < V) {
+                const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr[j]);
+                d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
+              }
+            }
+          },
+          out);
+    }
   };
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);

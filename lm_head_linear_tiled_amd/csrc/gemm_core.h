@@ -458,10 +458,18 @@ struct TileGemm {
     int q = 0;
     for (int j = 0;;) {
       for (int kt = 0; kt < KT; ++kt, ++q) {
-        wait_and_barrier<0>();
+        // After an epilogue only LDS work is drained: every wave waited for its
+        // copies of this slice before the epilogue, so the global stores the
+        // epilogue issued stay in flight.
+        if (kt == 0 && j > 0)
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+          wait_and_barrier<0>();
         slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pkb + pk * BK : KT * BK, acc);
         advance();
       }
+      // this wave's copies of the next tile's first slice have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
       if (!next_tile(next, ++j, tm0, tn0, tkb)) break;
       init(acc, tm0, tn0);
