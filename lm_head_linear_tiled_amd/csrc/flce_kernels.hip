@@ -112,27 +112,45 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
     return vt_begin + j < vt_end;
   };
   auto fold = [&](typename G::Acc& a, int m0, int, char*) {
+    // interior vocabulary tile: no row masks, and the max taken before the log2(e)
+    // scaling (a positive factor, so the same value)
+    const bool interior = m0 + kTile <= V;
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       float tmax = -INFINITY;
+      if (interior) {
 #pragma unroll
-      for (int i = 0; i < G::FM; ++i)
+        for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-          const float val = v < V ? a[i][j][r] * kLog2e : -INFINITY;
-          tmax = fmaxf(tmax, val);
-        }
-      const float mnew = fmaxf(mrun[j], tmax);
-      if (mnew != -INFINITY) {
-        float ssum = 0.f;
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, a[i][j][r]);
+        tmax *= kLog2e;
+      } else {
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
-            ssum += v < V ? __builtin_amdgcn_exp2f(a[i][j][r] * kLog2e - mnew) : 0.f;
+            const float val = v < V ? a[i][j][r] * kLog2e : -INFINITY;
+            tmax = fmaxf(tmax, val);
           }
+      }
+      const float mnew = fmaxf(mrun[j], tmax);
+      if (mnew != -INFINITY) {
+        float ssum = 0.f;
+        if (interior) {
+#pragma unroll
+          for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ssum += __builtin_amdgcn_exp2f(__builtin_fmaf(a[i][j][r], kLog2e, -mnew));
+        } else {
+#pragma unroll
+          for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+              ssum += v < V ? __builtin_amdgcn_exp2f(a[i][j][r] * kLog2e - mnew) : 0.f;
+            }
+        }
         srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - mnew) + ssum;
         mrun[j] = mnew;
       }
