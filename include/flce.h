@@ -38,6 +38,9 @@
  *     (FLCE_ERR_ALIAS), and the workspace may overlap nothing.
  *   - x and W base pointers must be 16-byte aligned and H * sizeof(dt) must be a
  *     multiple of 16 (FLCE_ERR_ALIGN otherwise).
+ *   - N, H and V lie in [1, 2^30]; H * sizeof(dt) and V (rounded up to 256) *
+ *     sizeof(dt) are at most 8 MiB (FLCE_ERR_SHAPE otherwise; workspace size
+ *     functions return 0).
  *   - Targets must lie in [0, V).  The kernels never read out of bounds for other
  *     values: such a token gets a NaN loss term and no one-hot term in D.
  *   - A status other than FLCE_OK means nothing was enqueued, except FLCE_ERR_HIP,

@@ -36,6 +36,14 @@ bool dims_ok(int64_t N, int64_t H, int64_t V) {
   return N > 0 && H > 0 && V > 0 && N <= kMaxDim && H <= kMaxDim && V <= kMaxDim;
 }
 bool dtype_ok(flce_dtype dt) { return dt == FLCE_F32 || dt == FLCE_BF16; }
+// A copy of a 256-row operand tile addresses its rows from one buffer resource
+// with a 2 GiB range, so a row (H entries of x or W, the padded V entries of a
+// dlogit panel) may span at most 8 MiB.
+bool rows_ok(int64_t H, int64_t V, flce_dtype dt) {
+  constexpr int64_t kMaxRowBytes = int64_t(8) << 20;
+  const int64_t es = (int64_t)esize(dt);
+  return H * es <= kMaxRowBytes && ceil_div(V, kTile) * kTile * es <= kMaxRowBytes;
+}
 
 FwdPlan plan_forward(int64_t N, int64_t V) {
   FwdPlan p{};
@@ -208,6 +216,7 @@ flce_status check_common(const void* x, const void* W, const int64_t* target, in
   if (!x || !W || !target) return FLCE_ERR_NULL;
   if (!dims_ok(N, H, V)) return FLCE_ERR_SHAPE;
   if (!dtype_ok(dt)) return FLCE_ERR_DTYPE;
+  if (!rows_ok(H, V, dt)) return FLCE_ERR_SHAPE;
   if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_REDUCTION;
   if (!aligned16(x) || !aligned16(W) || (H * (int64_t)esize(dt)) % 16 != 0) return FLCE_ERR_ALIGN;
   return FLCE_OK;
@@ -233,7 +242,9 @@ const char* flce_status_string(flce_status s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";
     case FLCE_ERR_NULL: return "FLCE_ERR_NULL: a required pointer is NULL";
-    case FLCE_ERR_SHAPE: return "FLCE_ERR_SHAPE: N, H and V must lie in [1, 2^30]";
+    case FLCE_ERR_SHAPE:
+      return "FLCE_ERR_SHAPE: N, H and V must lie in [1, 2^30], and H and V (rounded up to 256) times the element "
+             "size may not exceed 8 MiB";
     case FLCE_ERR_DTYPE: return "FLCE_ERR_DTYPE: unknown element type";
     case FLCE_ERR_REDUCTION: return "FLCE_ERR_REDUCTION: unknown reduction";
     case FLCE_ERR_ALIAS: return "FLCE_ERR_ALIAS: an output overlaps an input, another output or the workspace";
@@ -245,17 +256,17 @@ const char* flce_status_string(flce_status s) {
 }
 
 size_t flce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
-  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return plan_forward(N, V).total;
 }
 
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
-  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total;
 }
 
 size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
-  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return plan_backward_for(N, H, V, dt, int64_t(kTile) * kTile).total;
 }
 
@@ -329,7 +340,7 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
 }
 
 size_t flce_backward_chunked_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t chunk_tokens) {
-  if (!dims_ok(N, H, V) || !dtype_ok(dt) || chunk_tokens < 1) return 0;
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt) || chunk_tokens < 1) return 0;
   return plan_backward_chunked(N, H, V, dt, chunk_tokens).total;
 }
 
@@ -365,7 +376,7 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
 }
 
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
-  if (!dims_ok(N, H, V) || !dtype_ok(dt)) return 0;
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return 256 + std::max(plan_forward(N, V).total,
                         plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total);
 }

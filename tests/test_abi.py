@@ -186,3 +186,17 @@ def test_backward_plan_shapes(lib):
     # a single panel covers a smaller problem: no accumulators; its grad_x launches
     # would fill half the CUs, so their vocabulary is split in two (float32 partials)
     assert lib.flce_backward_workspace_bytes(2048, 4096, 32000, BF16) == 2048 * 32000 * 2 + 2 * 2048 * 4096 * 4
+
+
+def test_row_length_limits(lib):
+    """A 256-row operand tile is addressed through one 2 GiB buffer range, so rows of
+    more than 8 MiB (H of x and W, padded V of a dlogit panel) are refused."""
+    MiB = 1 << 20
+    assert lib.flce_forward_workspace_bytes(64, 4 * MiB, 1000, BF16) > 0      # 8 MiB rows: allowed
+    assert lib.flce_forward_workspace_bytes(64, 4 * MiB + 8, 1000, BF16) == 0
+    assert lib.flce_backward_workspace_bytes(64, 2 * MiB + 4, 1000, F32) == 0
+    assert lib.flce_backward_workspace_bytes(64, 128, 4 * MiB, BF16) > 0
+    assert lib.flce_backward_workspace_bytes(64, 128, 4 * MiB + 1, BF16) == 0  # padded to 256 entries
+    assert lib.flce_backward_chunked_workspace_bytes(64, 128, 2 * MiB + 1, F32, 256) == 0
+    assert fwd(lib, H=4 * MiB + 8, dt=BF16) == SHAPE
+    assert bwd(lib, V=2 * MiB + 1, nws=1 << 40) == SHAPE
