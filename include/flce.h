@@ -39,7 +39,8 @@
  *   - x and W base pointers must be 16-byte aligned and H * sizeof(dt) must be a
  *     multiple of 16 (FLCE_ERR_ALIGN otherwise).
  *   - N, H and V lie in [1, 2^30]; H * sizeof(dt) and V (rounded up to 256) *
- *     sizeof(dt) are at most 8 MiB (FLCE_ERR_SHAPE otherwise; workspace size
+ *     sizeof(dt) are at most 8 MiB; each of N x V, N x H and V x H has fewer
+ *     than 2^31 tiles of 256 x 256 (FLCE_ERR_SHAPE otherwise; workspace size
  *     functions return 0).
  *   - Targets must lie in [0, V).  The kernels never read out of bounds for other
  *     values: such a token gets a NaN loss term and no one-hot term in D.

@@ -32,8 +32,13 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t esize(flce_dtype dt) { return dt == FLCE_BF16 ? 2 : 4; }
 
+// Each size in [1, 2^30], and the 256 x 256 tiles of every contraction (N x V,
+// N x H, V x H) countable in 32 bits.
 bool dims_ok(int64_t N, int64_t H, int64_t V) {
-  return N > 0 && H > 0 && V > 0 && N <= kMaxDim && H <= kMaxDim && V <= kMaxDim;
+  if (!(N > 0 && H > 0 && V > 0 && N <= kMaxDim && H <= kMaxDim && V <= kMaxDim)) return false;
+  constexpr int64_t kMaxTiles = int64_t(1) << 31;
+  const int64_t tn = (N + 255) / 256, th = (H + 255) / 256, tv = (V + 255) / 256;
+  return tn * tv < kMaxTiles && tn * th < kMaxTiles && tv * th < kMaxTiles;
 }
 bool dtype_ok(flce_dtype dt) { return dt == FLCE_F32 || dt == FLCE_BF16; }
 // A copy of a 256-row operand tile addresses its rows from one buffer resource

@@ -199,4 +199,7 @@ def test_row_length_limits(lib):
     assert lib.flce_backward_workspace_bytes(64, 128, 4 * MiB + 1, BF16) == 0  # padded to 256 entries
     assert lib.flce_backward_chunked_workspace_bytes(64, 128, 2 * MiB + 1, F32, 256) == 0
     assert fwd(lib, H=4 * MiB + 8, dt=BF16) == SHAPE
+    # 2^22 token tiles x 2^9 vocabulary tiles = 2^31 logit tiles: not countable in 32 bits
+    assert lib.flce_forward_workspace_bytes(1 << 30, 128, 1 << 17, BF16) == 0
+    assert lib.flce_forward_workspace_bytes(1 << 30, 128, (1 << 17) - 256, BF16) > 0
     assert bwd(lib, V=2 * MiB + 1, nws=1 << 40) == SHAPE
