@@ -148,12 +148,39 @@ struct TileGemm {
   // (buffer_load ... lds: lane l of a wave instruction lands at M0 + 16 l); chunks
   // outside the valid range get an offset past the buffer bound, which the
   // hardware reads as zeros.  Completion is awaited by the barrier's vmcnt(0).
-  template <int MAJ, int MNT, int J0 = 0, int J1 = MNT * BK * ES / 1024 / NWAVES>
+  template <int MAJ, int MNT, int J0 = 0, int J1 = MNT * BK * ES / 1024 / NWAVES, bool LEAN = false>
   static __device__ __forceinline__ void load_tile(const Operand<T>& op, int mn0, int k0, T* lds_op) {
     constexpr int RB = row_bytes<MAJ, MNT>();
     constexpr int SLOTS = RB / 16;
     if constexpr (J0 >= J1) return;
-    const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+    const int l = (int)threadIdx.x & 63;
+    if constexpr (LEAN) {
+      // Whole K slice of a K-major operand (k0 + BK <= k_ext <= ld, checked by the
+      // caller): the descriptor starts at row mn0 (k = 0) and ends after its last
+      // valid row, so rows past mn_ext fail the range check and read zeros, and
+      // every other bound holds.  Copy j of a wave reads rows ROWS_J further down
+      // than copy j - 1 with the same swizzled slot, so its lane offset is the
+      // first one plus a scalar: no per-copy address math.
+      static_assert(MAJ == K_MAJOR, "lean copies are K-major");
+      constexpr int ROWS_J = NWAVES * 64 / SLOTS;
+      static_assert((NWAVES * 4) % (RB / 16) == 0, "copy j keeps the swizzled slot of copy 0");
+      const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
+      const int rows = op.mn_ext - mn0 < MNT ? op.mn_ext - mn0 : MNT;
+      const uint32_t num = rows > 0 ? (uint32_t)rows * ldb : 0u;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)mn0 * op.ld), (short)0, num, 0x00020000);
+      const int w = (int)threadIdx.x >> 6;
+      const int row0 = (J0 * NWAVES + w) * (64 / SLOTS) + l / SLOTS;
+      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
+      const int ws = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+      for (int j = J0; j < J1; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + (j * NWAVES + ws) * 1024), 16,
+            off0 + (uint32_t)((j - J0) * ROWS_J) * ldb, k0 * ES, 0, 0);
+      return;
+    }
+    const int w = (int)threadIdx.x >> 6;
     const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
@@ -263,21 +290,21 @@ struct TileGemm {
   }
 
   // Issue copy instructions [C0, C1) of the combined A-then-B sequence.
-  template <int C0, int C1>
+  template <int C0, int C1, bool LEAN>
   static __device__ __forceinline__ void load_part(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
                                                    T* stage) {
     constexpr int A0 = C0 < INSTR_A ? C0 : INSTR_A, A1 = C1 < INSTR_A ? C1 : INSTR_A;
     constexpr int B0 = (C0 > INSTR_A ? C0 : INSTR_A) - INSTR_A, B1 = (C1 > INSTR_A ? C1 : INSTR_A) - INSTR_A;
-    load_tile<AMAJ, BM, A0, A1>(A, m0, k0, stage);
-    load_tile<BMAJ, BN, B0, B1>(B, n0, k0, stage + A_BYTES / ES);
+    load_tile<AMAJ, BM, A0, A1, LEAN>(A, m0, k0, stage);
+    load_tile<BMAJ, BN, B0, B1, LEAN>(B, n0, k0, stage + A_BYTES / ES);
   }
 
-  template <int S>
+  template <int S, bool LEAN>
   static __device__ __forceinline__ void load_step(const Operand<T>& A, const Operand<T>& B, int m0, int n0, int k0,
                                                    T* stage) {
     constexpr int C0 = S * VPER < N_VMEM ? S * VPER : N_VMEM;
     constexpr int C1 = (S + 1) * VPER < N_VMEM ? (S + 1) * VPER : N_VMEM;
-    if constexpr (S < VSTEPS) load_part<C0, C1>(A, B, m0, n0, k0, stage);
+    if constexpr (S < VSTEPS) load_part<C0, C1, LEAN>(A, B, m0, n0, k0, stage);
   }
   static constexpr int vmem_in_step(int s) {
     return s < VSTEPS ? ((s + 1) * VPER < N_VMEM ? (s + 1) * VPER : N_VMEM) - (s * VPER < N_VMEM ? s * VPER : N_VMEM)
@@ -365,6 +392,7 @@ struct TileGemm {
   // copies are spread over the first fragment steps (DMA) or loaded at the first
   // step and written at the last (register staging), and the LDS fragment reads of
   // step s+1 are interleaved with the MFMAs of step s.
+  template <bool LEAN>
   static __device__ __forceinline__ void slice(const Operand<T>& A, const Operand<T>& B, T* lds, int cur, int pm0,
                                                int pn0, int pk0, Acc& acc) {
     constexpr int STAGE = STAGE_BYTES / ES;
@@ -390,7 +418,7 @@ struct TileGemm {
           rstore<BN, 0, N_VMEM - INSTR_A>(nstage + AOFF, rg + INSTR_A);
         }
       } else {
-        load_step<s>(A, B, pm0, pn0, pk0, nstage);
+        load_step<s, LEAN>(A, B, pm0, pn0, pk0, nstage);
       }
       if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
@@ -434,6 +462,23 @@ struct TileGemm {
   template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
                                                    Next&& next, Epi&& epi, Init&& init) {
+    // Lean copies (load_tile) when both operands are K-major and DMA-copied and
+    // every slice is a whole K slice: tiles start at K offset 0 and K is a
+    // multiple of BK inside both K ranges, each K range inside its rows.
+    constexpr bool LEAN_OK = STAGING == STAGE_DMA && AMAJ == K_MAJOR && BMAJ == K_MAJOR &&
+                             !std::is_invocable_v<Next&, int, int&, int&, int&>;
+    if constexpr (LEAN_OK) {
+      if (K % BK == 0 && K <= A.k_ext && K <= B.k_ext && A.k_ext <= A.ld && B.k_ext <= B.ld) {
+        run_tiles_impl<true>(A, B, K, lds, acc, next, epi, init);
+        return;
+      }
+    }
+    run_tiles_impl<false>(A, B, K, lds, acc, next, epi, init);
+  }
+
+  template <bool LEAN, class Next, class Epi, class Init>
+  static __device__ __forceinline__ void run_tiles_impl(const Operand<T>& A, const Operand<T>& B, int K, T* lds,
+                                                        Acc& acc, Next&& next, Epi&& epi, Init&& init) {
     static_assert(NSTAGE == 2, "the persistent loop double-buffers K slices");
     constexpr int AOFF = A_BYTES / ES;
     const int KT = (K + BK - 1) / BK;
@@ -465,7 +510,10 @@ struct TileGemm {
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else
           wait_and_barrier<0>();
-        slice(A, B, lds, q & 1, pm0, pn0, pvalid ? pkb + pk * BK : KT * BK, acc);
+        // past the last tile the copies go to a stage no slice reads: lean ones
+        // re-read K offset 0 (inside the operands), the others K offset KT * BK,
+        // where every chunk fails its bounds check and reads zeros
+        slice<LEAN>(A, B, lds, q & 1, pm0, pn0, pvalid ? pkb + pk * BK : (LEAN ? 0 : KT * BK), acc);
         advance();
       }
       // this wave's copies of the next tile's first slice have landed
