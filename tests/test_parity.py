@@ -99,6 +99,16 @@ def test_grad_x_split_k_several_panels(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_x_sums_over_wide_panels(gpu, dtype):
+    """grad_x over two vocabulary panels of many K slices each, split in K: later
+    panels start from the earlier panels' float32 sums; ragged tokens and hidden
+    size (H = 320: the second hidden tile is mostly past H)."""
+    N, H, V = 300, 320, 12000
+    nws = gpu.backward_workspace_bytes(N, H, V, torch.float32 if dtype == "f32" else torch.bfloat16) // 2
+    check_case(gpu, N, H, V, dtype, "sum", seed=23, grad_loss=0.7, bwd_ws_bytes=nws)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_w_zero_closed_form(gpu, dtype):
     """W = 0: lse = ln V and loss = ln V (mean), grad_x = 0 exactly."""
     N, H, V = 200, 64, 777
