@@ -597,7 +597,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
                           part + (int64_t)s * Ncp * H, row_ok, row_local);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Ks, lds, acc, next, store, init);
+  if (ks == 1) {
+    // one split: tiles start at K offset 0, which lets whole-slice copies take
+    // the lean form
+    auto next1 = [&](int j, int& m0, int& n0) {
+      int s;
+      return item(j, s, m0, n0);
+    };
+    G::run_tiles(A, B, Ks, lds, acc, next1, store, init);
+  } else {
+    G::run_tiles(A, B, Ks, lds, acc, next, store, init);
+  }
 }
 
 // Sum of the ks float32 partial grad_x row blocks [Kc, H] (fixed order) into

@@ -260,11 +260,45 @@ struct TileGemm {
 
   // Register-staged copies: buffer loads (out-of-range lanes read zeros) into
   // registers, written to the same swizzled LDS slots later.
-  template <int MAJ, int MNT, int J0, int J1>
+  template <int MAJ, int MNT, int J0, int J1, bool LEAN = false>
   static __device__ __forceinline__ void rload(const Operand<T>& op, int mn0, int k0, u32x4_t* r) {
     constexpr int RB = row_bytes<MAJ, MNT>();
     constexpr int SLOTS = RB / 16;
     if constexpr (J0 >= J1) return;
+    if constexpr (LEAN) {
+      // As the lean DMA copies (load_tile): one lane offset, copy j ROWS_J storage
+      // rows further.  K-major: rows past mn_ext fail the descriptor's range
+      // check; MN-major (whole tile inside mn_ext, whole K slice): every chunk is
+      // inside the operand.
+      constexpr int ROWS_J = NWAVES * 64 / SLOTS;
+      static_assert(MAJ == K_MAJOR ? ROWS_J % (256 / RB) == 0 && (ROWS_J / (256 / RB)) % (RB / 16) == 0
+                                   : ROWS_J % (ES == 2 ? 4 : 2) == 0,
+                    "copy j keeps the swizzled slot of copy 0");
+      const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+      const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
+      __amdgpu_buffer_rsrc_t rsrc;
+      uint32_t soff;
+      if constexpr (MAJ == K_MAJOR) {
+        const int rows = op.mn_ext - mn0 < MNT ? op.mn_ext - mn0 : MNT;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)mn0 * op.ld), (short)0,
+                                                 rows > 0 ? (uint32_t)rows * ldb : 0u, 0x00020000);
+        soff = (uint32_t)(k0 * ES);
+      } else {
+        // the tile's BK rows of MNT elements; none if it lies past mn_ext (the
+        // copy cursor's origin past the last tile)
+        const bool in = mn0 + MNT <= op.mn_ext;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)k0 * op.ld + mn0), (short)0,
+                                                 in ? (uint32_t)(BK - 1) * ldb + MNT * ES : 0u, 0x00020000);
+        soff = 0;
+      }
+      const int row0 = (J0 * NWAVES + w) * (64 / SLOTS) + l / SLOTS;
+      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
+#pragma unroll
+      for (int j = J0; j < J1; ++j)
+        r[j - J0] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off0 + (uint32_t)((j - J0) * ROWS_J) * ldb, soff, 0));
+      return;
+    }
     const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
     const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
@@ -410,8 +444,8 @@ struct TileGemm {
       constexpr int s = decltype(sc)::value;
       if constexpr (STAGING == STAGE_REG) {
         if constexpr (s == 0) {
-          rload<AMAJ, BM, 0, INSTR_A>(A, pm0, pk0, rg);
-          rload<BMAJ, BN, 0, N_VMEM - INSTR_A>(B, pn0, pk0, rg + INSTR_A);
+          rload<AMAJ, BM, 0, INSTR_A, LEAN>(A, pm0, pk0, rg);
+          rload<BMAJ, BN, 0, N_VMEM - INSTR_A, LEAN>(B, pn0, pk0, rg + INSTR_A);
         }
         if constexpr (s == NSTEP - 1) {
           rstore<BM, 0, INSTR_A>(nstage, rg);
@@ -462,13 +496,18 @@ struct TileGemm {
   template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
                                                    Next&& next, Epi&& epi, Init&& init) {
-    // Lean copies (load_tile) when both operands are K-major and DMA-copied and
-    // every slice is a whole K slice: tiles start at K offset 0 and K is a
-    // multiple of BK inside both K ranges, each K range inside its rows.
-    constexpr bool LEAN_OK = STAGING == STAGE_DMA && AMAJ == K_MAJOR && BMAJ == K_MAJOR &&
+    // Lean copies (load_tile, rload) when every slice is a whole K slice -- tiles
+    // start at K offset 0 and K is a multiple of BK inside both K ranges -- and
+    // each operand is either K-major with its K range inside its rows, or (register
+    // staging only) MN-major with every tile inside its mn range.
+    constexpr bool LEAN_OK = (STAGING == STAGE_REG || (AMAJ == K_MAJOR && BMAJ == K_MAJOR)) &&
                              !std::is_invocable_v<Next&, int, int&, int&, int&>;
+    auto fits = [&](const Operand<T>& op, bool kmajor, int MNT) {
+      if (op.k_ext < K) return false;
+      return kmajor ? op.k_ext <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
+    };
     if constexpr (LEAN_OK) {
-      if (K % BK == 0 && K <= A.k_ext && K <= B.k_ext && A.k_ext <= A.ld && B.k_ext <= B.ld) {
+      if (K % BK == 0 && fits(A, AMAJ == K_MAJOR, BM) && fits(B, BMAJ == K_MAJOR, BN)) {
         run_tiles_impl<true>(A, B, K, lds, acc, next, epi, init);
         return;
       }
