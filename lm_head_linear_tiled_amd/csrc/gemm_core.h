@@ -346,12 +346,13 @@ struct TileGemm {
   }
 
   // One scheduling pattern per fragment step: after each of the step's N_MFMA
-  // MFMAs, first up to two of the NR LDS reads (the next step's fragments, so they
-  // are in flight as early as possible), then, once those are placed, the NV
-  // global loads / DMA copies and the NW LDS writes spread over the remaining MFMAs.
+  // MFMAs, first up to RPER of the NR LDS reads (the next step's fragments, so
+  // they are in flight as early as possible), then, once those are placed, the NV
+  // global loads / DMA copies and the NW LDS writes spread over the remaining
+  // MFMAs.  RPER: 3 with DMA copies, 2 with register staging (measured best).
   template <int NR, int NV, int NW>
   static __device__ __forceinline__ void schedule_step() {
-    constexpr int RPER = 2;
+    constexpr int RPER = STAGING == STAGE_DMA ? 3 : 2;
     constexpr int QR = (NR + RPER - 1) / RPER;              // MFMA slots taken by the reads
     constexpr int REST = N_MFMA - QR > 0 ? N_MFMA - QR : 1;  // slots left for the rest
     constexpr int VPER_ = (NV + REST - 1) / REST;
