@@ -35,22 +35,60 @@ class Timing(ctypes.Structure):
                 ("kinds", ctypes.POINTER(ctypes.c_int)), ("n_launches", ctypes.c_int)]
 
 
+_hip = None
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: hipEventDisableSystemFence
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime torch has already loaded (libflce.so resolves to the same one)."""
+    global _hip
+    if _hip is None:
+        torch.cuda.init()
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip = hip
+    return _hip
+
+
 class KernelTimer:
-    """Per-kernel durations of one library call, from torch-created HIP events."""
+    """Per-kernel durations of one library call, from HIP events recorded between its
+    kernels.  The events skip the system-scope fence that default events apply on
+    every record (timing only; the caller's synchronize makes results visible).
+    Measured on the headline step: default events lengthened it by 0.2-1.3 % depending
+    on the machine, these by at most 0.1 % against no events."""
 
     def __init__(self, n_events: int, device=None):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
-        for e in self.events:  # the HIP event is created on first record
-            e.record()
-        torch.cuda.synchronize(device)
-        self._handles = (ctypes.c_void_p * n_events)(*[e.cuda_event for e in self.events])
+        hip = _hip_runtime()
+        self.events = []
+        for _ in range(n_events):
+            ev = ctypes.c_void_p()
+            code = hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+            if code != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed with HIP error {code}")
+            self.events.append(ev.value)
+        self._handles = (ctypes.c_void_p * n_events)(*self.events)
         self._kinds = (ctypes.c_int * max(1, n_events - 1))()
         self.t = Timing(self._handles, n_events, self._kinds, 0)
+
+    def _elapsed(self, a, b) -> float:
+        ms = ctypes.c_float()
+        code = _hip_runtime().hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if code != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed with HIP error {code}")
+        return ms.value
 
     def durations(self):
         """[(kernel name, ms)] for every launch that got an event (call after a sync)."""
         n = min(self.t.n_launches, len(self.events) - 1)
-        return [(KERNEL_NAMES[self._kinds[k]], self.events[k].elapsed_time(self.events[k + 1])) for k in range(n)]
+        return [(KERNEL_NAMES[self._kinds[k]], self._elapsed(self.events[k], self.events[k + 1])) for k in range(n)]
+
+    def __del__(self):
+        hip = _hip
+        if hip is not None:
+            for ev in getattr(self, "events", []):
+                hip.hipEventDestroy(ev)
 
 
 class FLCEError(RuntimeError):
