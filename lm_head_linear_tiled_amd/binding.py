@@ -56,8 +56,8 @@ class KernelTimer:
     """Per-kernel durations of one library call, from HIP events recorded between its
     kernels.  The events skip the system-scope fence that default events apply on
     every record (timing only; the caller's synchronize makes results visible).
-    Measured on the headline step: default events lengthened it by 0.2-1.3 % depending
-    on the machine, these by at most 0.1 % against no events."""
+    Measured on the headline step against no events: default events lengthened it by
+    up to 1.3 % depending on the machine, these by at most run-to-run noise."""
 
     def __init__(self, n_events: int, device=None):
         hip = _hip_runtime()
