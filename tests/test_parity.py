@@ -99,6 +99,14 @@ def test_grad_x_split_k_several_panels(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_whole_slice_copies_with_ragged_rows(gpu, dtype):
+    """Tokens a multiple of the K slice but not of the tile (N = 320, H = 256): the
+    forward and dlogits copy x and W by whole K slices with rows past N and V left
+    to the buffer range check, and grad_W runs its whole-slice loop over K = 320."""
+    check_case(gpu, 320, 256, 3000, dtype, "sum", seed=24, grad_loss=1.25)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_grad_x_sums_over_wide_panels(gpu, dtype):
     """grad_x over two vocabulary panels of many K slices each, split in K: later
     panels start from the earlier panels' float32 sums; ragged tokens and hidden
