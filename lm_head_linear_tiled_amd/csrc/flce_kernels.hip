@@ -279,6 +279,13 @@ __device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n,
   return true;
 }
 
+// The dlogit kernel splits its waves into copy waves and store waves (its panel
+// stores then drain while the next tile runs).
+#ifndef FLCE_SPLIT_DLOGITS
+#define FLCE_SPLIT_DLOGITS 1
+#endif
+constexpr bool kSplitDlogits = FLCE_SPLIT_DLOGITS != 0;
+
 // Tile groups of the dlogit and grad_x launches: 8 rows (vocabulary tiles of W,
 // hidden tiles of W) per group, measured better there than 4.
 #ifndef FLCE_GROUP_M_WIDE
@@ -306,14 +313,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 //                    v = 16 bytes: elements m .. of row n, as S
 // LDS slots are XOR-swizzled so that the writes (32 lanes of different n) and the
 // reads (whole rows) are free of bank conflicts.  Starts with a workgroup barrier.
-template <typename S, int FM, int FN, class Val, class Out>
+// PAIRW = 0: every wave stores its own sub-tile, out(n, m, v).  PAIRW = the
+// workgroup's wave count: only the second half of the waves store, wave w the
+// sub-tiles of waves w - PAIRW / 2 and w, handed over through LDS (a barrier
+// after each round's writes and between rounds), out(src, n, m, v) with src the
+// wave whose sub-tile it is.
+template <typename S, int FM, int FN, int PAIRW = 0, class Val, class Out>
 __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& out) {
   static_assert(FM == 2 && FN == 4, "64 x 128 wave sub-tile");
   constexpr bool BF = sizeof(S) == 2;
   constexpr int RB = 64 * (int)sizeof(S);  // bytes of one output row of the sub-tile
   constexpr int TR = 8192 / RB;            // rows per round: 64 (bf16) or 32 (fp32)
   constexpr int JR = TR / 32;              // accumulator column blocks per round
-  const int l = (int)threadIdx.x & 63;
+  // The lane id is hidden from the optimiser here, so the per-lane row offsets
+  // below are recomputed in each epilogue instead of being kept live across the
+  // tile loop: kept, they are spilled, and every reload from scratch memory waits
+  // for all of the wave's outstanding global stores.
+  int l = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
   char* sc = spare + ((int)threadIdx.x >> 6) * 8192;
   // every wave has read its last fragments from spare (the copies still in flight
   // go to the other stage, so no vmcnt wait here)
@@ -342,21 +359,36 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
           }
         }
     }
+    // read back whole output rows of one wave's region and store them
+    auto drain = [&](const char* src_sc, auto&& put) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      int row, k;
-      uint4 v;
-      if constexpr (BF) {
-        row = q * 8 + (l >> 3);
-        k = l & 7;
-        v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
-        if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-      } else {
-        row = q * 4 + (l >> 4);
-        k = l & 15;
-        v = *reinterpret_cast<const uint4*>(sc + row * RB + ((k ^ (row & 15)) * 16));
+      for (int q = 0; q < 8; ++q) {
+        int row, k;
+        uint4 v;
+        if constexpr (BF) {
+          row = q * 8 + (l >> 3);
+          k = l & 7;
+          v = *reinterpret_cast<const uint4*>(src_sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
+          if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        } else {
+          row = q * 4 + (l >> 4);
+          k = l & 15;
+          v = *reinterpret_cast<const uint4*>(src_sc + row * RB + ((k ^ (row & 15)) * 16));
+        }
+        put(rd * TR + row, k * (16 / (int)sizeof(S)), v);
       }
-      out(rd * TR + row, k * (16 / (int)sizeof(S)), v);
+    };
+    if constexpr (PAIRW == 0) {
+      drain(sc, out);
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave's round is in LDS
+      const int w = (int)threadIdx.x >> 6;
+      if (w >= PAIRW / 2) {
+        const int w0 = w - PAIRW / 2;
+        drain(spare + w0 * 8192, [&](int n, int m, uint4 v) { out(w0, n, m, v); });
+        drain(sc, [&](int n, int m, uint4 v) { out(w, n, m, v); });
+      }
+      if (rd + 1 < FN / JR) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // read before rewritten
     }
   }
 }
@@ -372,8 +404,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
                                                         const float* __restrict__ grad_loss, float red_scale, int N,
                                                         int H, int V, int i0, int v0, int tiles_v, int tiles_t,
                                                         int Vbp, T* __restrict__ panel) {
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_DMA,
+                   kSplitDlogits>
+      G;
   static_assert(G::WM == 64 && G::STAGE_BYTES >= G::NWAVES * 8192, "dlogit staging layout");
+  constexpr int PAIRW = kSplitDlogits ? G::NWAVES : 0;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int l = (int)threadIdx.x & 63;
   const int wm = G::wave_m(), wn = G::wave_n();
@@ -406,30 +441,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
       lr[j] = tv[j] ? lv * kLog2e : 0.f;
       tt[j] = tv[j] && t64 >= 0 && t64 < V ? (int)t64 : -1;
     }
-    auto out = [&](int n, int m, uint4 v) {
-      *reinterpret_cast<uint4*>(panel + (int64_t)(tw + n - i0) * Vbp + (vw - v0) + m) = v;
+    // src: the wave whose sub-tile (rows from m0 + WM (src / WGN), tokens from
+    // n0 + WN (src % WGN)) the 16 bytes belong to
+    auto out = [&](int src, int n, int m, uint4 v) {
+      const int vs = m0 + (src / G::WGN) * G::WM, ts = n0 + (src % G::WGN) * G::WN;
+      *reinterpret_cast<uint4*>(panel + (int64_t)(ts + n - i0) * Vbp + (vs - v0) + m) = v;
     };
+    auto out_own = [&](int n, int m, uint4 v) { out((int)threadIdx.x >> 6, n, m, v); };
     if (m0 + kTile <= V && n0 + kTile <= N) {
       // interior tile: no masks; the one-hot term as -s at the target row, found
       // from the target's row offset lt within this lane's rows of the group
       int lt[G::FN];
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
-      staged_epilogue<T, G::FM, G::FN>(
-          spare,
-          [&](int i, int j, int g, float* d) {
+      auto val = [&](int i, int j, int g, float* d) {
             const int r = lt[j] - (i * 32 + 8 * g);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lr[j]));
               d[u] = __builtin_fmaf(s, p, r == u ? -s : 0.f);
             }
-          },
-          out);
+          };
+      if constexpr (PAIRW > 0)
+        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out);
+      else
+        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own);
     } else {
-      staged_epilogue<T, G::FM, G::FN>(
-          spare,
-          [&](int i, int j, int g, float* d) {
+      auto val = [&](int i, int j, int g, float* d) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
@@ -439,8 +477,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
                 d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
               }
             }
-          },
-          out);
+          };
+      if constexpr (PAIRW > 0)
+        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out);
+      else
+        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own);
     }
   };
   typename G::Acc acc;
@@ -485,7 +526,8 @@ __device__ __forceinline__ void grad_init(typename G::Acc& acc, int hw, int nw, 
     G::zero(acc);
     return;
   }
-  const int l = (int)threadIdx.x & 63;
+  int l = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(l));  // recomputed offsets, as in staged_epilogue
 #pragma unroll
   for (int j = 0; j < G::FN; ++j) {
     const int n = nw + j * 32 + (l & 31);
@@ -707,6 +749,30 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       hipLaunchKernelGGL(bwd_dlogits<T>, grid(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
                          red_scale, N, H, V, i0, v0, tiles_n, tiles_m, Vbp, panel);
       rec.after(FLCE_K_BWD_DLOGITS);
+#ifdef FLCE_GX_FIRST
+      // grad_x rows of this chunk accumulate over vocabulary panels; a launch with
+      // few output tiles splits the panel's vocabulary (partial sums in gx_part).
+      constexpr int BK = Cfg<T>::BK;
+      const int Ks = (int)((((int64_t)Kv + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
+      const int ks = (Kv + Ks - 1) / Ks;
+      const int acc_x = pv > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
+      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc,
+                         Kv, W, H, N, i0, v0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x);
+      rec.after(FLCE_K_BWD_GRAD_X);
+      if (ks > 1) {
+        const int64_t n4 = (int64_t)Kc * H / 4;
+        const int rgrid = (int)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)p.max_workgroups);
+        hipLaunchKernelGGL(bwd_gx_reduce<T>, dim3(rgrid), dim3(256), 0, st, (const float*)gx_part, ks,
+                           (int64_t)p.Ncp * H, Kc, H, i0, fin_x, gx, gxa);
+        rec.after(FLCE_K_BWD_GX_REDUCE);
+      }
+      // grad_W rows of this panel accumulate over token chunks.
+      float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
+      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
+                         V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
+                         c == p.n_chunks - 1 ? 1 : 0);
+      rec.after(FLCE_K_BWD_GRAD_W);
+#else
       // grad_W rows of this panel accumulate over token chunks.
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
       hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
@@ -729,6 +795,7 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
                            (int64_t)p.Ncp * H, Kc, H, i0, fin_x, gx, gxa);
         rec.after(FLCE_K_BWD_GX_REDUCE);
       }
+#endif
     }
   }
   const hipError_t e = hipGetLastError();

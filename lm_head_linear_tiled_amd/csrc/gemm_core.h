@@ -110,14 +110,21 @@ enum Staging {
   STAGE_REG = 1   // 16-byte buffer loads into registers, then ds_write_b128
 };
 
+// SPLIT (DMA staging only): the first half of the waves issue every K-slice copy
+// and are the only ones that wait for copies; the second half issue none, so
+// global stores they leave in flight (an epilogue's) are never waited for by the
+// tile loop -- the memory counter that copies are awaited with also counts
+// stores, in issue order.
 template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ, int NSTAGE_ = 2, int WGM_ = 2, int WGN_ = 2,
-          int STAGING = STAGE_DMA>
+          int STAGING = STAGE_DMA, bool SPLIT = false>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int NSTAGE = NSTAGE_;  // LDS stages: NSTAGE - 1 K slices in flight
   static constexpr int WGM = WGM_, WGN = WGN_;  // wave grid over the tile
   static constexpr int NWAVES = WGM * WGN;
   static constexpr int NT = 64 * NWAVES;
+  static constexpr int NCW = SPLIT ? NWAVES / 2 : NWAVES;  // waves that issue copies
+  static_assert(!SPLIT || STAGING == STAGE_DMA, "split copy/store waves need DMA staging");
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VEC = ElemTraits<T>::VEC;
   static constexpr int KSTEP = ElemTraits<T>::KSTEP;
@@ -132,7 +139,10 @@ struct TileGemm {
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   static constexpr int LDS_ELEMS = LDS_BYTES / ES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(A_BYTES % (NWAVES * 1024) == 0 && B_BYTES % (NWAVES * 1024) == 0, "whole 1 KiB wave loads");
+  static_assert(A_BYTES % (NCW * 1024) == 0 && B_BYTES % (NCW * 1024) == 0, "whole 1 KiB wave loads");
+
+  // Does this wave issue K-slice copies?  (wave-uniform)
+  static __device__ __forceinline__ bool copy_wave() { return !SPLIT || ((int)threadIdx.x >> 6) < NCW; }
 
   static __device__ __forceinline__ int wave_m() { return ((int)threadIdx.x >> 6) / WGN; }
   static __device__ __forceinline__ int wave_n() { return ((int)threadIdx.x >> 6) % WGN; }
@@ -148,7 +158,7 @@ struct TileGemm {
   // (buffer_load ... lds: lane l of a wave instruction lands at M0 + 16 l); chunks
   // outside the valid range get an offset past the buffer bound, which the
   // hardware reads as zeros.  Completion is awaited by the barrier's vmcnt(0).
-  template <int MAJ, int MNT, int J0 = 0, int J1 = MNT * BK * ES / 1024 / NWAVES, bool LEAN = false>
+  template <int MAJ, int MNT, int J0 = 0, int J1 = MNT * BK * ES / 1024 / NCW, bool LEAN = false>
   static __device__ __forceinline__ void load_tile(const Operand<T>& op, int mn0, int k0, T* lds_op) {
     constexpr int RB = row_bytes<MAJ, MNT>();
     constexpr int SLOTS = RB / 16;
@@ -162,21 +172,21 @@ struct TileGemm {
       // than copy j - 1 with the same swizzled slot, so its lane offset is the
       // first one plus a scalar: no per-copy address math.
       static_assert(MAJ == K_MAJOR, "lean copies are K-major");
-      constexpr int ROWS_J = NWAVES * 64 / SLOTS;
-      static_assert((NWAVES * 4) % (RB / 16) == 0, "copy j keeps the swizzled slot of copy 0");
+      constexpr int ROWS_J = NCW * 64 / SLOTS;
+      static_assert((NCW * 4) % (RB / 16) == 0, "copy j keeps the swizzled slot of copy 0");
       const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
       const int rows = op.mn_ext - mn0 < MNT ? op.mn_ext - mn0 : MNT;
       const uint32_t num = rows > 0 ? (uint32_t)rows * ldb : 0u;
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)mn0 * op.ld), (short)0, num, 0x00020000);
       const int w = (int)threadIdx.x >> 6;
-      const int row0 = (J0 * NWAVES + w) * (64 / SLOTS) + l / SLOTS;
+      const int row0 = (J0 * NCW + w) * (64 / SLOTS) + l / SLOTS;
       const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
       const int ws = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
       for (int j = J0; j < J1; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + (j * NWAVES + ws) * 1024), 16,
+            rsrc, (__attribute__((address_space(3))) void*)((char*)lds_op + (j * NCW + ws) * 1024), 16,
             off0 + (uint32_t)((j - J0) * ROWS_J) * ldb, k0 * ES, 0, 0);
       return;
     }
@@ -185,7 +195,7 @@ struct TileGemm {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
     for (int j = J0; j < J1; ++j) {
-      const int blk = j * NWAVES + w;  // 1 KiB block of the tile
+      const int blk = j * NCW + w;  // 1 KiB block of the tile
       const int chunk = blk * 64 + l;
       const int row = chunk / SLOTS;
       const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
@@ -248,7 +258,7 @@ struct TileGemm {
   static constexpr int DS_B = (BMAJ == MN_MAJOR && ES == 2) ? 2 : 1;
   static constexpr int N_DS = FM * DS_A + FN * DS_B;
   static constexpr int N_MFMA = FM * FN;
-  static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / NWAVES;
+  static constexpr int N_VMEM = (BM + BN) * BK * ES / 1024 / NCW;
 
   // The copies of one K slice (A's then B's wave instructions, N_VMEM in all) are
   // spread over the first VSTEPS fragment steps, VPER per step, so that the eight
@@ -256,7 +266,7 @@ struct TileGemm {
   static constexpr int NSTEP_ = BK / KSTEP;
   static constexpr int VSTEPS = NSTEP_ > 1 ? NSTEP_ - 1 : 1;
   static constexpr int VPER = (N_VMEM + VSTEPS - 1) / VSTEPS;
-  static constexpr int INSTR_A = BM * BK * ES / 1024 / NWAVES;
+  static constexpr int INSTR_A = BM * BK * ES / 1024 / NCW;
 
   // Register-staged copies: buffer loads (out-of-range lanes read zeros) into
   // registers, written to the same swizzled LDS slots later.
@@ -409,8 +419,10 @@ struct TileGemm {
     static_assert(N >= 0 && N < 64, "vmcnt");
     if constexpr (STAGING == STAGE_REG)  // the staged ds_writes must also have landed
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-    else
+    else if (copy_wave())
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    else
+      asm volatile("s_barrier" ::: "memory");
   }
 
   static __device__ __forceinline__ void zero(Acc& acc) {
@@ -427,7 +439,7 @@ struct TileGemm {
   // copies are spread over the first fragment steps (DMA) or loaded at the first
   // step and written at the last (register staging), and the LDS fragment reads of
   // step s+1 are interleaved with the MFMAs of step s.
-  template <bool LEAN>
+  template <bool LEAN, bool COPY = true>
   static __device__ __forceinline__ void slice(const Operand<T>& A, const Operand<T>& B, T* lds, int cur, int pm0,
                                                int pn0, int pk0, Acc& acc) {
     constexpr int STAGE = STAGE_BYTES / ES;
@@ -452,7 +464,7 @@ struct TileGemm {
           rstore<BM, 0, INSTR_A>(nstage, rg);
           rstore<BN, 0, N_VMEM - INSTR_A>(nstage + AOFF, rg + INSTR_A);
         }
-      } else {
+      } else if constexpr (COPY) {
         load_step<s, LEAN>(A, B, pm0, pn0, pk0, nstage);
       }
       if constexpr (s + 1 < NSTEP) load_frags(as, bs, wm, wn, (s + 1) * KSTEP, fa[(s + 1) & 1], fb[(s + 1) & 1]);
@@ -464,7 +476,7 @@ struct TileGemm {
       if constexpr (STAGING == STAGE_REG)
         schedule_step<NR, s == 0 ? N_VMEM : 0, s == NSTEP - 1 ? N_VMEM : 0>();
       else
-        schedule_step<NR, vmem_in_step(s), 0>();
+        schedule_step<NR, COPY ? vmem_in_step(s) : 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
     });
   }
@@ -529,8 +541,11 @@ struct TileGemm {
     // slice reads) stay inside the operands or read zeros
     int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0, pkb = tkb;
     bool pvalid = true;
-    load_tile<AMAJ, BM>(A, pm0, pkb, lds);
-    load_tile<BMAJ, BN>(B, pn0, pkb, lds + AOFF);
+    const bool cw = copy_wave();
+    if (cw) {
+      load_tile<AMAJ, BM>(A, pm0, pkb, lds);
+      load_tile<BMAJ, BN>(B, pn0, pkb, lds + AOFF);
+    }
     auto advance = [&]() {
       if (++pk == KT) {
         pk = 0;
@@ -553,11 +568,16 @@ struct TileGemm {
         // past the last tile the copies go to a stage no slice reads: lean ones
         // re-read K offset 0 (inside the operands), the others K offset KT * BK,
         // where every chunk fails its bounds check and reads zeros
-        slice<LEAN>(A, B, lds, q & 1, pm0, pn0, pvalid ? pkb + pk * BK : (LEAN ? 0 : KT * BK), acc);
+        const int pk0 = pvalid ? pkb + pk * BK : (LEAN ? 0 : KT * BK);
+        if (!SPLIT || cw)
+          slice<LEAN>(A, B, lds, q & 1, pm0, pn0, pk0, acc);
+        else
+          slice<LEAN, false>(A, B, lds, q & 1, pm0, pn0, pk0, acc);
         advance();
       }
-      // this wave's copies of the next tile's first slice have landed
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // this wave's copies of the next tile's first slice have landed (a wave
+      // without copies leaves its stores in flight)
+      if (cw) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
       if (!next_tile(next, ++j, tm0, tn0, tkb)) break;
       init(acc, tm0, tn0);
