@@ -26,6 +26,10 @@ constexpr int kFwdTargetWorkgroups = FLCE_FWD_TARGET_WGS;  // forward workgroups
 #define FLCE_PANEL_MB 128
 #endif
 constexpr size_t kDefaultPanelBytes = size_t(FLCE_PANEL_MB) << 20;  // dlogit panel budget
+#ifndef FLCE_PANEL_GROUP
+#define FLCE_PANEL_GROUP 2
+#endif
+constexpr int kPanelGroup = FLCE_PANEL_GROUP;  // panels per grad_x launch when all tokens form one chunk (1 or 2)
 constexpr int kPlanCUs = 256;  // compute units the panel shape is planned for (MI355X)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -71,7 +75,8 @@ FwdPlan plan_forward(int64_t N, int64_t V) {
   return p;
 }
 
-BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb);
+BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb,
+                            int group = 1);
 
 // grad_x K splits for chunks of Nc tokens and panels of Vb entries: when a
 // grad_x launch has fewer output tiles than half the compute units, its K
@@ -121,7 +126,14 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
 // of least estimated time; accumulators only where a gradient is summed over
 // several launches.  (Also trying narrower panels that fill whole rounds of the
 // compute units was measured no better.)
-BwdPlan plan_backward_for(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t panel_elems) {
+//
+// group = 2 (used when every token fits in one chunk and there are several
+// panels): two consecutive panels are kept in the panel buffer, one block each,
+// the dlogit and grad_W launches still work one panel at a time, and grad_x runs
+// once per pair over both blocks: half the float32 accumulator passes over
+// grad_x (each a burst of loads at the start and of stores at the end of a
+// launch) for one more panel of workspace.
+BwdPlan plan_backward_for(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t panel_elems, int group = 1) {
   const int64_t Np = ceil_div(N, kTile) * kTile;
   const int64_t Vp = ceil_div(V, kTile) * kTile;
   int64_t best_nc = kTile, best_vb = kTile;
@@ -136,12 +148,13 @@ BwdPlan plan_backward_for(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_
       best_vb = Vb;
     }
   }
-  return plan_backward_shape(N, H, V, dt, best_nc, best_vb);
+  const bool one_chunk = best_nc >= N, several_panels = best_vb < V;
+  return plan_backward_shape(N, H, V, dt, best_nc, best_vb, one_chunk && several_panels ? group : 1);
 }
 
 // Plan for chunks of Nc tokens and panels of Vb vocabulary entries (both
 // multiples of kTile, at most the padded N and V).
-BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb) {
+BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int64_t Nc, int64_t Vb, int group) {
   BwdPlan p{};
   p.Nc = (int)Nc;
   p.Ncp = (int)Nc;  // a multiple of kTile
@@ -149,15 +162,16 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   p.Vb = (int)Vb;
   p.Vbp = (int)Vb;  // a multiple of kTile
   p.n_panels = (int)ceil_div(V, Vb);
+  p.gx_group = std::max(1, std::min(group, std::min(p.n_panels, 2)));
   const size_t es = esize(dt);
   // float32 gradients accumulate in place; bfloat16 ones through float32 buffers.
   p.gx_bytes = (dt == FLCE_BF16 && p.n_panels > 1) ? sizeof(float) * (size_t)N * H : 0;
   p.gw_bytes = (dt == FLCE_BF16 && p.n_chunks > 1) ? sizeof(float) * (size_t)Vb * H : 0;
-  p.gx_splits = (int)gx_splits_for(Nc, Vb, H);
+  p.gx_splits = (int)gx_splits_for(Nc, std::min<int64_t>((int64_t)p.gx_group * Vb, V), H);
   p.gxpart_bytes = p.gx_splits > 1 ? sizeof(float) * (size_t)p.gx_splits * p.Ncp * H : 0;
   size_t o = 0;
   p.off_panel = o;
-  o = align_up(o + es * (size_t)p.Ncp * p.Vbp, 256);
+  o = align_up(o + es * (size_t)p.Ncp * p.Vbp * p.gx_group, 256);
   p.off_gx = o;
   o = align_up(o + p.gx_bytes, 256);
   p.off_gw = o;
@@ -168,15 +182,18 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   return p;
 }
 
-// Largest panel (up to the default budget) whose plan fits in ws_bytes.
+// Largest panel (up to the default budget) whose plan fits in ws_bytes; at each
+// panel size the grouped plan first.
 bool plan_backward(int64_t N, int64_t H, int64_t V, flce_dtype dt, size_t ws_bytes, BwdPlan* out) {
   int64_t elems = (int64_t)(kDefaultPanelBytes / esize(dt));
   const int64_t min_elems = int64_t(kTile) * kTile;
   while (true) {
-    BwdPlan p = plan_backward_for(N, H, V, dt, elems);
-    if (p.total <= ws_bytes) {
-      *out = p;
-      return true;
+    for (int group : {kPanelGroup, 1}) {
+      BwdPlan p = plan_backward_for(N, H, V, dt, elems, group);
+      if (p.total <= ws_bytes) {
+        *out = p;
+        return true;
+      }
     }
     if (elems <= min_elems) return false;
     elems = std::max(min_elems, elems / 2);
@@ -267,7 +284,7 @@ size_t flce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype 
 
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
   if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
-  return plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total;
+  return plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt)), kPanelGroup).total;
 }
 
 size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
@@ -383,7 +400,7 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
   if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return 256 + std::max(plan_forward(N, V).total,
-                        plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt))).total);
+                        plan_backward_for(N, H, V, dt, (int64_t)(kDefaultPanelBytes / esize(dt)), kPanelGroup).total);
 }
 
 flce_status flce_forward_backward(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H,

@@ -584,13 +584,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
 
 // grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
 // vocabulary][m = hidden], MN-major), cols = chunk tokens (B = the panel as [n =
-// token][k = vocabulary], K-major); written as grad_x rows i0 + n.  With ks > 1
+// token][k = vocabulary], K-major; Kgp padded columns, the ones past Vbp in a
+// second panel block); written as grad_x rows i0 + n.  With ks > 1
 // the panel's vocabulary is split into ks ranges of Ks entries: work item
 // (split s, tile) covers range s and writes its float32 partial sums to
 // part + s * Ncp * H (rows chunk-local); split 0 starts from the sums of earlier
 // panels; bwd_gx_reduce adds the splits.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kc, int Kv,
+__global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kgp, int Kc, int Kv,
                                                        const T* __restrict__ W, int H, int N, int i0, int v0,
                                                        int tiles_h, int tiles_t, int ks, int Ks, int Ncp,
                                                        T* __restrict__ gx_out, float* __restrict__ gx_acc,
@@ -600,7 +601,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int wm = G::wave_m(), wn = G::wave_n();
   const Operand<T> A{W + (int64_t)v0 * H, H, H, Kv};
-  const Operand<T> B{panel, Vbp, Kc, Vbp};
+  // a pair of panels: the second block starts Ncp * Vbp elements further and holds
+  // K offsets Vbp .. Kgp - 1
+  const Operand<T> B{panel, Vbp, Kc, Kgp, Kgp > Vbp ? Vbp : 0x7fffffff, (int64_t)Ncp * Vbp};
   const int tiles = tiles_h * tiles_t;
   // the j-th work item of this workgroup: split s, tile origin (m0, n0)
   auto item = [&](int j, int& s, int& m0, int& n0) {
@@ -740,6 +743,14 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
     const int v0 = pv * p.Vb;
     const int Kv = min(p.Vb, V - v0);
     const int Vbp = p.Vbp;
+    // panel pv goes to block g of the panel buffer (gx_group > 1 only with one
+    // token chunk); grad_x runs after the last panel of each group
+    const int g = pv % p.gx_group;
+    T* sub = panel + (int64_t)g * p.Ncp * Vbp;
+    const bool gx_now = g == p.gx_group - 1 || pv == p.n_panels - 1;
+    const int gv0 = (pv - g) * p.Vb;                          // first vocabulary entry of the group
+    const int Kg = v0 + Kv - gv0;                             // its entries
+    const int Kgp = g * Vbp + (Kv + kTile - 1) / kTile * kTile;  // its padded columns
     for (int c = 0; c < p.n_chunks; ++c) {
       const int i0 = c * p.Nc;
       const int Kc = min(p.Nc, N - i0);
@@ -747,17 +758,24 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int tiles_n = (Kv + kTile - 1) / kTile;
       auto grid = [&](int tiles) { return dim3(min(tiles, p.max_workgroups)); };
       hipLaunchKernelGGL(bwd_dlogits<T>, grid(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
-                         red_scale, N, H, V, i0, v0, tiles_n, tiles_m, Vbp, panel);
+                         red_scale, N, H, V, i0, v0, tiles_n, tiles_m, Vbp, sub);
       rec.after(FLCE_K_BWD_DLOGITS);
-#ifdef FLCE_GX_FIRST
-      // grad_x rows of this chunk accumulate over vocabulary panels; a launch with
-      // few output tiles splits the panel's vocabulary (partial sums in gx_part).
+      // grad_W rows of this panel accumulate over token chunks.
+      float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
+      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)sub, Vbp, Kc, x,
+                         H, V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
+                         c == p.n_chunks - 1 ? 1 : 0);
+      rec.after(FLCE_K_BWD_GRAD_W);
+      if (!gx_now) continue;
+      // grad_x rows of this chunk accumulate over panel groups; a launch with
+      // few output tiles splits the group's vocabulary (partial sums in gx_part).
       constexpr int BK = Cfg<T>::BK;
-      const int Ks = (int)((((int64_t)Kv + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
-      const int ks = (Kv + Ks - 1) / Ks;
-      const int acc_x = pv > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
-      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc,
-                         Kv, W, H, N, i0, v0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x);
+      const int Ks = (int)((((int64_t)Kg + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
+      const int ks = (Kg + Ks - 1) / Ks;
+      const int acc_x = gv0 > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
+      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp,
+                         Kgp, Kc, Kg, W, H, N, i0, gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x,
+                         fin_x);
       rec.after(FLCE_K_BWD_GRAD_X);
       if (ks > 1) {
         const int64_t n4 = (int64_t)Kc * H / 4;
@@ -766,36 +784,6 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
                            (int64_t)p.Ncp * H, Kc, H, i0, fin_x, gx, gxa);
         rec.after(FLCE_K_BWD_GX_REDUCE);
       }
-      // grad_W rows of this panel accumulate over token chunks.
-      float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
-      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
-                         V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
-                         c == p.n_chunks - 1 ? 1 : 0);
-      rec.after(FLCE_K_BWD_GRAD_W);
-#else
-      // grad_W rows of this panel accumulate over token chunks.
-      float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
-      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc, x, H,
-                         V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
-                         c == p.n_chunks - 1 ? 1 : 0);
-      rec.after(FLCE_K_BWD_GRAD_W);
-      // grad_x rows of this chunk accumulate over vocabulary panels; a launch with
-      // few output tiles splits the panel's vocabulary (partial sums in gx_part).
-      constexpr int BK = Cfg<T>::BK;
-      const int Ks = (int)((((int64_t)Kv + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
-      const int ks = (Kv + Ks - 1) / Ks;
-      const int acc_x = pv > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
-      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp, Kc,
-                         Kv, W, H, N, i0, v0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x);
-      rec.after(FLCE_K_BWD_GRAD_X);
-      if (ks > 1) {
-        const int64_t n4 = (int64_t)Kc * H / 4;
-        const int rgrid = (int)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)p.max_workgroups);
-        hipLaunchKernelGGL(bwd_gx_reduce<T>, dim3(rgrid), dim3(256), 0, st, (const float*)gx_part, ks,
-                           (int64_t)p.Ncp * H, Kc, H, i0, fin_x, gx, gxa);
-        rec.after(FLCE_K_BWD_GX_REDUCE);
-      }
-#endif
     }
   }
   const hipError_t e = hipGetLastError();

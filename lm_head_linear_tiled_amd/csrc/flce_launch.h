@@ -23,6 +23,7 @@ struct FwdPlan {
 struct BwdPlan {
   int Nc, n_chunks;         // tokens per chunk, chunks
   int Vb, Vbp, n_panels;    // vocabulary per panel, padded, panels
+  int gx_group;             // panels kept in the panel buffer (one [Ncp, Vbp] block each); grad_x runs once per group
   int Ncp;                  // Nc padded to kTile
   int gx_splits;            // grad_x K splits per launch (1: none), partial sums in gxpart
   size_t off_panel, off_gx, off_gw, off_gxpart, total;  // workspace carving (bytes); 0-sized parts unused

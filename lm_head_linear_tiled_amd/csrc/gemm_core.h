@@ -63,13 +63,25 @@ struct ElemTraits<float> {
   static constexpr int KSTEP = 2;
 };
 
-// A strided view of one contraction operand.
+// A strided view of one contraction operand, optionally in two blocks along K:
+// k >= ksplit lives at ptr + jump as the view of k - ksplit (ksplit a multiple
+// of the K slice, so no slice straddles it).
 template <typename T>
 struct Operand {
   const T* ptr;  // element (mn = 0, k = 0)
   int64_t ld;    // elements between consecutive storage rows
   int mn_ext;    // rows/cols [0, mn_ext) are valid
   int k_ext;     // k in [0, k_ext) is valid
+  int ksplit = 0x7fffffff;
+  int64_t jump = 0;
+  // origin of the block holding K offset k0 (wave-uniform), k0 made block-relative
+  __device__ __forceinline__ const T* block(int& k0) const {
+    if (k0 >= ksplit) {
+      k0 -= ksplit;
+      return ptr + jump;
+    }
+    return ptr;
+  }
 };
 
 // float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
@@ -177,8 +189,9 @@ struct TileGemm {
       const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
       const int rows = op.mn_ext - mn0 < MNT ? op.mn_ext - mn0 : MNT;
       const uint32_t num = rows > 0 ? (uint32_t)rows * ldb : 0u;
+      const T* const org = op.block(k0);
       const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)mn0 * op.ld), (short)0, num, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)(org + (int64_t)mn0 * op.ld), (short)0, num, 0x00020000);
       const int w = (int)threadIdx.x >> 6;
       const int row0 = (J0 * NCW + w) * (64 / SLOTS) + l / SLOTS;
       const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
@@ -191,7 +204,9 @@ struct TileGemm {
       return;
     }
     const int w = (int)threadIdx.x >> 6;
-    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
+    const int kg = k0;  // K offset for the bounds check
+    const T* const org = op.block(k0);
+    const T* base = MAJ == K_MAJOR ? org + (int64_t)mn0 * op.ld + k0 : org + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
     for (int j = J0; j < J1; ++j) {
@@ -200,7 +215,7 @@ struct TileGemm {
       const int row = chunk / SLOTS;
       const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
       const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
-      const int k = MAJ == K_MAJOR ? k0 + slot * VEC : k0 + row;
+      const int k = MAJ == K_MAJOR ? kg + slot * VEC : kg + row;
       const bool ok = mn < op.mn_ext && k < op.k_ext;
       const uint32_t off = (uint32_t)(((int64_t)row * op.ld + slot * VEC) * ES);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -286,18 +301,19 @@ struct TileGemm {
                     "copy j keeps the swizzled slot of copy 0");
       const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
       const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
+      const T* const org = op.block(k0);
       __amdgpu_buffer_rsrc_t rsrc;
       uint32_t soff;
       if constexpr (MAJ == K_MAJOR) {
         const int rows = op.mn_ext - mn0 < MNT ? op.mn_ext - mn0 : MNT;
-        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)mn0 * op.ld), (short)0,
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(org + (int64_t)mn0 * op.ld), (short)0,
                                                  rows > 0 ? (uint32_t)rows * ldb : 0u, 0x00020000);
         soff = (uint32_t)(k0 * ES);
       } else {
         // the tile's BK rows of MNT elements; none if it lies past mn_ext (the
         // copy cursor's origin past the last tile)
         const bool in = mn0 + MNT <= op.mn_ext;
-        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(op.ptr + (int64_t)k0 * op.ld + mn0), (short)0,
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(org + (int64_t)k0 * op.ld + mn0), (short)0,
                                                  in ? (uint32_t)(BK - 1) * ldb + MNT * ES : 0u, 0x00020000);
         soff = 0;
       }
@@ -310,7 +326,9 @@ struct TileGemm {
       return;
     }
     const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
-    const T* base = MAJ == K_MAJOR ? op.ptr + (int64_t)mn0 * op.ld + k0 : op.ptr + (int64_t)k0 * op.ld + mn0;
+    const int kg = k0;  // K offset for the bounds check
+    const T* const org = op.block(k0);
+    const T* base = MAJ == K_MAJOR ? org + (int64_t)mn0 * op.ld + k0 : org + (int64_t)k0 * op.ld + mn0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
     for (int j = J0; j < J1; ++j) {
@@ -319,7 +337,7 @@ struct TileGemm {
       const int row = chunk / SLOTS;
       const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
       const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
-      const int k = MAJ == K_MAJOR ? k0 + slot * VEC : k0 + row;
+      const int k = MAJ == K_MAJOR ? kg + slot * VEC : kg + row;
       const bool ok = mn < op.mn_ext && k < op.k_ext;
       const uint32_t off = (uint32_t)(((int64_t)row * op.ld + slot * VEC) * ES);
       r[j - J0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? off : 0x80000000u, 0, 0));
@@ -517,7 +535,8 @@ struct TileGemm {
                              !std::is_invocable_v<Next&, int, int&, int&, int&>;
     auto fits = [&](const Operand<T>& op, bool kmajor, int MNT) {
       if (op.k_ext < K) return false;
-      return kmajor ? op.k_ext <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
+      const int k1 = op.k_ext < op.ksplit ? op.k_ext : op.ksplit;  // K extent of the first block
+      return kmajor ? k1 <= op.ld && op.k_ext - k1 <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
     };
     if constexpr (LEAN_OK) {
       if (K % BK == 0 && fits(A, AMAJ == K_MAJOR, BM) && fits(B, BMAJ == K_MAJOR, BN)) {

@@ -117,6 +117,29 @@ def test_grad_x_sums_over_wide_panels(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_x_over_panel_pairs(gpu, dtype):
+    """All tokens in one chunk and several vocabulary panels (the default
+    workspace): two panels are kept at once, each in its own block, and grad_x runs
+    once per pair with its copies crossing from the first block to the second; the
+    odd, ragged last panel forms a group of its own.  One grad_x output tile, so
+    each group's vocabulary is split in K and the ranges cross the block boundary."""
+    N, H, V = 200, 72, 600000
+    got = check_case(gpu, N, H, V, dtype, "mean", seed=25, grad_loss=1.1)
+    x, W, t = make_inputs(N, H, V, dtype, seed=25)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(64)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.1], device="cuda"), "mean", timer=bt)
+    torch.cuda.synchronize()
+    panels = 3 if dtype == "bf16" else 5  # 128 MB panels of 256 (padded) tokens: 262144 / 131072 entries
+    seq = []
+    for p in range(panels):
+        seq += ["bwd_dlogits", "bwd_grad_w"]
+        if p % 2 == 1 or p == panels - 1:
+            seq += ["bwd_grad_x", "bwd_gx_reduce"]
+    assert [k for k, _ in bt.durations()] == seq
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_w_zero_closed_form(gpu, dtype):
     """W = 0: lse = ln V and loss = ln V (mean), grad_x = 0 exactly."""
     N, H, V = 200, 64, 777
