@@ -29,7 +29,7 @@ constexpr size_t kDefaultPanelBytes = size_t(FLCE_PANEL_MB) << 20;  // dlogit pa
 #ifndef FLCE_PANEL_GROUP
 #define FLCE_PANEL_GROUP 2
 #endif
-constexpr int kPanelGroup = FLCE_PANEL_GROUP;  // panels per grad_x launch when all tokens form one chunk (1 or 2)
+constexpr int kPanelGroup = FLCE_PANEL_GROUP;  // panels per grad_x launch when all tokens form one chunk
 constexpr int kPlanCUs = 256;  // compute units the panel shape is planned for (MI355X)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -162,7 +162,7 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   p.Vb = (int)Vb;
   p.Vbp = (int)Vb;  // a multiple of kTile
   p.n_panels = (int)ceil_div(V, Vb);
-  p.gx_group = std::max(1, std::min(group, std::min(p.n_panels, 2)));
+  p.gx_group = std::max(1, std::min(group, p.n_panels));
   const size_t es = esize(dt);
   // float32 gradients accumulate in place; bfloat16 ones through float32 buffers.
   p.gx_bytes = (dt == FLCE_BF16 && p.n_panels > 1) ? sizeof(float) * (size_t)N * H : 0;
@@ -188,7 +188,8 @@ bool plan_backward(int64_t N, int64_t H, int64_t V, flce_dtype dt, size_t ws_byt
   int64_t elems = (int64_t)(kDefaultPanelBytes / esize(dt));
   const int64_t min_elems = int64_t(kTile) * kTile;
   while (true) {
-    for (int group : {kPanelGroup, 1}) {
+    for (int group : {kPanelGroup, 2, 1}) {
+      if (group > kPanelGroup) continue;
       BwdPlan p = plan_backward_for(N, H, V, dt, elems, group);
       if (p.total <= ws_bytes) {
         *out = p;

@@ -584,8 +584,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
 
 // grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
 // vocabulary][m = hidden], MN-major), cols = chunk tokens (B = the panel as [n =
-// token][k = vocabulary], K-major; Kgp padded columns, the ones past Vbp in a
-// second panel block); written as grad_x rows i0 + n.  With ks > 1
+// token][k = vocabulary], K-major; Kgp padded columns, each Vbp of them in a
+// panel block of their own); written as grad_x rows i0 + n.  With ks > 1
 // the panel's vocabulary is split into ks ranges of Ks entries: work item
 // (split s, tile) covers range s and writes its float32 partial sums to
 // part + s * Ncp * H (rows chunk-local); split 0 starts from the sums of earlier
@@ -601,8 +601,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int wm = G::wave_m(), wn = G::wave_n();
   const Operand<T> A{W + (int64_t)v0 * H, H, H, Kv};
-  // a pair of panels: the second block starts Ncp * Vbp elements further and holds
-  // K offsets Vbp .. Kgp - 1
+  // a group of panels: block b starts b Ncp Vbp elements further and holds K
+  // offsets b Vbp .. (b + 1) Vbp - 1 (the last one up to Kgp - 1)
   const Operand<T> B{panel, Vbp, Kc, Kgp, Kgp > Vbp ? Vbp : 0x7fffffff, (int64_t)Ncp * Vbp};
   const int tiles = tiles_h * tiles_t;
   // the j-th work item of this workgroup: split s, tile origin (m0, n0)

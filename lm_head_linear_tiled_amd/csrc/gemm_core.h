@@ -63,9 +63,9 @@ struct ElemTraits<float> {
   static constexpr int KSTEP = 2;
 };
 
-// A strided view of one contraction operand, optionally in two blocks along K:
-// k >= ksplit lives at ptr + jump as the view of k - ksplit (ksplit a multiple
-// of the K slice, so no slice straddles it).
+// A strided view of one contraction operand, optionally in blocks along K: K
+// offsets [b ksplit, (b + 1) ksplit) live at ptr + b jump as the view of
+// k - b ksplit (ksplit a multiple of the K slice, so no slice straddles a block).
 template <typename T>
 struct Operand {
   const T* ptr;  // element (mn = 0, k = 0)
@@ -76,11 +76,12 @@ struct Operand {
   int64_t jump = 0;
   // origin of the block holding K offset k0 (wave-uniform), k0 made block-relative
   __device__ __forceinline__ const T* block(int& k0) const {
-    if (k0 >= ksplit) {
+    const T* p = ptr;
+    while (k0 >= ksplit) {
       k0 -= ksplit;
-      return ptr + jump;
+      p += jump;
     }
-    return ptr;
+    return p;
   }
 };
 
@@ -535,8 +536,8 @@ struct TileGemm {
                              !std::is_invocable_v<Next&, int, int&, int&, int&>;
     auto fits = [&](const Operand<T>& op, bool kmajor, int MNT) {
       if (op.k_ext < K) return false;
-      const int k1 = op.k_ext < op.ksplit ? op.k_ext : op.ksplit;  // K extent of the first block
-      return kmajor ? k1 <= op.ld && op.k_ext - k1 <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
+      const int k1 = op.k_ext < op.ksplit ? op.k_ext : op.ksplit;  // K extent of the widest block
+      return kmajor ? k1 <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
     };
     if constexpr (LEAN_OK) {
       if (K % BK == 0 && fits(A, AMAJ == K_MAJOR, BM) && fits(B, BMAJ == K_MAJOR, BN)) {
