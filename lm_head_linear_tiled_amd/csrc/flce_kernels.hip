@@ -318,8 +318,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // sub-tiles of waves w - PAIRW / 2 and w, handed over through LDS (a barrier
 // after each round's writes and between rounds), out(src, n, m, v) with src the
 // wave whose sub-tile it is.
-template <typename S, int FM, int FN, int PAIRW = 0, class Val, class Out>
-__device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& out) {
+//   fix(j, tb, poke): called for each column block j of a round after its values
+//   are in LDS (tb: the block's first row of the round); poke(t, m, x) replaces
+//   the element of row t of the round, M index m, of this lane's own region by x.
+template <typename S, int FM, int FN, int PAIRW = 0, class Val, class Out, class Fix>
+__device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& out, Fix&& fix) {
   static_assert(FM == 2 && FN == 4, "64 x 128 wave sub-tile");
   constexpr bool BF = sizeof(S) == 2;
   constexpr int RB = 64 * (int)sizeof(S);  // bytes of one output row of the sub-tile
@@ -359,6 +362,18 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
           }
         }
     }
+    auto poke = [&](int t, int m, float x) {
+      if constexpr (BF) {
+        const int slot = (m >> 3) ^ ((t >> 1) & 7);
+        const int half = ((m >> 2) & 1) ^ ((t >> 4) & 1);
+        *reinterpret_cast<bf16_t*>(sc + t * RB + slot * 16 + half * 8 + 2 * (m & 3)) = f32_to_bf16(x);
+      } else {
+        const int slot = (m >> 2) ^ (t & 15);
+        *reinterpret_cast<float*>(sc + t * RB + slot * 16 + 4 * (m & 3)) = x;
+      }
+    };
+#pragma unroll
+    for (int jj = 0; jj < JR; ++jj) fix(rd * JR + jj, jj * 32, poke);
     // read back whole output rows of one wave's region and store them
     auto drain = [&](const char* src_sc, auto&& put) {
 #pragma unroll
@@ -391,6 +406,10 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
       if (rd + 1 < FN / JR) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // read before rewritten
     }
   }
+}
+template <typename S, int FM, int FN, int PAIRW = 0, class Val, class Out>
+__device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& out) {
+  staged_epilogue<S, FM, FN, PAIRW>(spare, val, out, [](int, int, auto&&) {});
 }
 
 
@@ -449,23 +468,47 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
     };
     auto out_own = [&](int n, int m, uint4 v) { out((int)threadIdx.x >> 6, n, m, v); };
     if (m0 + kTile <= V && n0 + kTile <= N) {
-      // interior tile: no masks; the one-hot term as -s at the target row, found
-      // from the target's row offset lt within this lane's rows of the group
+      // interior tile, no masks: s exp2(a log2e - l) = +-exp2(a log2e - (l - log2|s|)),
+      // so each element costs an fma, an exp2 and a sign flip; the one-hot term of
+      // the target element (one per token column, in at most one lane of one wave)
+      // is patched into the staged values afterwards, computed as before:
+      // fma(s, p, -s).  s = 0 gives exp2(-inf) = 0.
+      const float ls = __builtin_amdgcn_logf(__builtin_fabsf(s));
+      const uint32_t sbit = __float_as_uint(s) & 0x80000000u;
+      float lrs[G::FN];
       int lt[G::FN];
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
+      for (int j = 0; j < G::FN; ++j) {
+        lrs[j] = lr[j] - ls;
+        // target row offset within this wave's rows of this lane's half
+        lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
+      }
       auto val = [&](int i, int j, int g, float* d) {
-            const int r = lt[j] - (i * 32 + 8 * g);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lr[j]));
-              d[u] = __builtin_fmaf(s, p, r == u ? -s : 0.f);
-            }
-          };
+        for (int u = 0; u < 4; ++u)
+          d[u] = __uint_as_float(
+              __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lrs[j]))) ^ sbit);
+      };
+      auto fix = [&](int j, int tb, auto&& poke) {
+        const int r = lt[j];
+        const bool hit = r >= 0 && r < G::WM && (r & 4) == 0;
+        if (!__any(hit)) return;
+        if (hit) {
+          // acc[i][j][4 g + u] with i = r / 32, g = r / 8 % 4, u = r % 4
+          const int want = (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
+          float a = 0.f;
+#pragma unroll
+          for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) a = want == i * 16 + q ? acc[i][j][q] : a;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(a, kLog2e, -lr[j]));
+          poke(tb + (l & 31), r + 4 * (l >> 5), __builtin_fmaf(s, p, -s));
+        }
+      };
       if constexpr (PAIRW > 0)
-        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out);
+        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out, fix);
       else
-        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own);
+        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own, fix);
     } else {
       auto val = [&](int i, int j, int g, float* d) {
 #pragma unroll
