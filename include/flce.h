@@ -105,10 +105,12 @@ flce_status flce_forward(const void* x, const void* W, const int64_t* target, in
 
 /* Bytes of device workspace flce_backward needs for these sizes (a pure function
  * of its arguments; 0 for invalid arguments): the dlogit panel of its default
- * plan (at most 128 MB, its shape chosen for these sizes) plus float32
- * accumulators where a gradient is summed over several panels or token chunks.
- * A smaller workspace, down to flce_backward_min_workspace_bytes, makes the
- * backward use smaller panels (more passes); a larger one changes nothing. */
+ * plan (at most 128 MiB, its shape chosen for these sizes), two of them when all
+ * tokens form one chunk and the vocabulary takes several panels (grad_x then runs
+ * once per pair), plus float32 accumulators where a gradient is summed over
+ * several launches.  A smaller workspace, down to
+ * flce_backward_min_workspace_bytes, makes the backward keep one panel at a time
+ * or use smaller panels (more passes); a larger one changes nothing. */
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
 size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
 
@@ -168,7 +170,7 @@ typedef enum {
   FLCE_K_FWD_LOSS = 2,    /* block sums -> scalar loss                             */
   FLCE_K_BWD_DLOGITS = 3, /* logit tile recompute -> dlogit panel                   */
   FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
-  FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel              */
+  FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel or a pair    */
   FLCE_K_FILL = 6,        /* writes the implicit grad_loss of 1                    */
   FLCE_K_BWD_GX_REDUCE = 7 /* adds the K-split partial sums of a grad_x launch       */
 } flce_kernel;
