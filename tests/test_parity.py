@@ -217,12 +217,26 @@ def test_deterministic(gpu, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_grad_loss_linear(gpu, dtype):
+    """Edge tiles only (N = 130 < one token tile): there D = s (p - onehot) is formed
+    in fp32 and then rounded, and a power-of-two scale commutes with every rounding.
+    (Interior tiles fold s into the exponent; test_negative_and_zero_grad_loss.)"""
     N, H, V = 130, 64, 300
     x, W, t = make_inputs(N, H, V, dtype, seed=12)
     a = run_hip(gpu, x, W, t, dtype, "sum", grad_loss=1.0)
     b = run_hip(gpu, x, W, t, dtype, "sum", grad_loss=-0.25)
-    # D is formed in fp32 then rounded; a power-of-two scale commutes with every rounding
     assert np.array_equal(b["gx"], -0.25 * a["gx"]) and np.array_equal(b["gW"], -0.25 * a["gW"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("grad_loss", [-0.6, 0.0])
+def test_negative_and_zero_grad_loss(gpu, dtype, grad_loss):
+    """Every tile inside N and V: the dlogit scale enters the exponent as
+    log2|grad_loss| and its sign as a sign flip, the one-hot term is patched in
+    afterwards; a zero upstream gradient gives exactly zero gradients."""
+    N, H, V = 512, 256, 1024
+    got = check_case(gpu, N, H, V, dtype, "mean", seed=31, grad_loss=grad_loss)
+    if grad_loss == 0.0:
+        assert not np.any(got["gx"]) and not np.any(got["gW"])
 
 
 def test_autograd_matches_direct(gpu):
