@@ -34,6 +34,9 @@ def parse():
                     help="panels: flce_backward (bounded dlogit panels, the default); chunked: "
                          "flce_backward_chunked, token chunks over the whole vocabulary, for comparison")
     ap.add_argument("--chunk-tokens", type=int, default=1024, help="tokens per chunk for --backward chunked")
+    ap.add_argument("--workspace-mb", type=float, default=None,
+                    help="backward workspace in MiB instead of the library's default size (the planner then "
+                         "uses the largest dlogit panels whose plan fits)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), to scale the HBM counters")
     return ap.parse_args()
@@ -85,11 +88,22 @@ def cpu_baseline(x, W, t, dtype, H, V, target_s):
 
     import oracle
     from lm_head_linear_tiled_amd.inputs import widen
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas")
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(int(i.get("num_threads", 1)) for i in info)
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})" for i in info)
     except Exception:  # threadpoolctl missing: fall back to the affinity mask
         cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     Wf = widen(W, dtype)
 
     def run(n):
@@ -109,6 +123,7 @@ def cpu_baseline(x, W, t, dtype, H, V, target_s):
         secs = run(n)
     tflops = 8.0 * n * H * V / secs / 1e12
     return {"value": round(tflops, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"{n} of {len(t)} tokens x full V={V}, H={H}: oracle.forward then oracle.backward "
                       f"(float64 numpy, logits materialised per token chunk), {secs:.1f} s",
             "seconds": round(secs, 2), "tokens": n}
@@ -149,6 +164,8 @@ def main():
         nbws = binding.backward_chunked_workspace_bytes(N, H, V, tdt, args.chunk_tokens)
     else:
         nbws = binding.backward_workspace_bytes(N, H, V, tdt)
+    if args.workspace_mb is not None:
+        nbws = int(args.workspace_mb * (1 << 20))
     bws = torch.empty(nbws, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -173,8 +190,10 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
+    res = None
     for k in range(args.steps):
-        loss, gx, gW = step(ftimers[k], btimers[k])
+        res = None  # a step's outputs are dropped before the next step allocates its own
+        res = step(ftimers[k], btimers[k])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -189,7 +208,14 @@ def main():
     f1.record()
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
+    # peak device memory of one step on its own: inputs, workspaces and that step's outputs
+    res = None
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    res = step()
+    torch.cuda.synchronize()
     peak_mem = torch.cuda.max_memory_allocated()
+    res = None
 
     # per-kernel durations from the events recorded inside the timed steps
     per = {}
@@ -242,6 +268,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(dom, args.workload),
+                     "traffic_scope": "bytes past the L2 (L2 misses, last-level-cache hits included): rocprofv3 "
+                                      "FETCH_SIZE and WRITE_SIZE per launch, scaled by what they read for a plain "
+                                      "1 GiB device copy",
                      "flops_per_launch": flops_per_launch, "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:

@@ -72,6 +72,27 @@ def _check(x: np.ndarray, W: np.ndarray, target: np.ndarray, reduction: str):
     return t.astype(np.int64)
 
 
+def _check_rows(x: np.ndarray, W: np.ndarray, target, idx, n_idx: int, what: str):
+    """Shape and target checks of the per-row helpers (as ``_check``, no reduction):
+    targets outside [0, V) raise instead of wrapping around in numpy indexing."""
+    if x.ndim != 2 or W.ndim != 2 or x.shape[1] != W.shape[1]:
+        raise OracleError(f"x {x.shape} and W {W.shape} must be [N,H] and [V,H]")
+    N, V = x.shape[0], W.shape[0]
+    if N == 0 or V == 0:
+        raise OracleError("N and V must be positive")
+    t = np.asarray(target)
+    if t.shape != (N,) or not np.issubdtype(t.dtype, np.integer):
+        raise OracleError(f"target must be an integer vector of length {N}")
+    if t.min() < 0 or t.max() >= V:
+        raise OracleError("target outside [0, V)")
+    idx = np.asarray(idx)
+    if idx.ndim != 1 or not np.issubdtype(idx.dtype, np.integer):
+        raise OracleError(f"{what} must be an integer vector")
+    if idx.size and (idx.min() < 0 or idx.max() >= n_idx):
+        raise OracleError(f"{what} outside [0, {n_idx})")
+    return t.astype(np.int64), idx.astype(np.int64)
+
+
 def _chunk_rows(V: int) -> int:
     return max(1, _CHUNK_BYTES // (8 * max(V, 1)))
 
@@ -144,8 +165,7 @@ def backward(x, W, target, reduction: str = "mean", grad_loss: float = 1.0):
 def forward_rows(x, W, target, rows):
     """(lse, target_logit) for the selected token rows only."""
     x, W = _as_f64(x), _as_f64(W)
-    t = np.asarray(target, dtype=np.int64)
-    rows = np.asarray(rows, dtype=np.int64)
+    t, rows = _check_rows(x, W, target, rows, x.shape[0], "rows")
     z = logits(x[rows], W)
     return log_sum_exp(z), z[np.arange(len(rows)), t[rows]]
 
@@ -153,8 +173,9 @@ def forward_rows(x, W, target, rows):
 def grad_x_rows(x, W, target, rows, reduction: str = "mean", grad_loss: float = 1.0):
     """grad_x for the selected token rows; each row needs only its own logits."""
     x, W = _as_f64(x), _as_f64(W)
-    t = np.asarray(target, dtype=np.int64)
-    rows = np.asarray(rows, dtype=np.int64)
+    t, rows = _check_rows(x, W, target, rows, x.shape[0], "rows")
+    if reduction not in ("mean", "sum"):
+        raise OracleError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
     s = scale_of(reduction, x.shape[0], grad_loss)
     z = logits(x[rows], W)
     return dlogits(z, log_sum_exp(z), t[rows], s) @ W
@@ -166,8 +187,11 @@ def grad_w_rows(x, W, target, vrows, lse, reduction: str = "mean", grad_loss: fl
     grad_W[v] = s * sum_i (exp(z_iv - lse_i) - [t_i == v]) x_i.
     """
     x, W = _as_f64(x), _as_f64(W)
-    t = np.asarray(target, dtype=np.int64)
-    vrows = np.asarray(vrows, dtype=np.int64)
+    t, vrows = _check_rows(x, W, target, vrows, W.shape[0], "vrows")
+    if reduction not in ("mean", "sum"):
+        raise OracleError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
+    if np.shape(lse) != (x.shape[0],):
+        raise OracleError(f"lse must have one value per token ({x.shape[0]})")
     s = scale_of(reduction, x.shape[0], grad_loss)
     zc = x @ W[vrows].T                      # [N, len(vrows)]
     P = np.exp(zc - np.asarray(lse, dtype=np.float64)[:, None])

@@ -6,8 +6,12 @@ import numpy as np
 import torch
 
 TOL = {
-    # fp32 inputs: loss relative 1e-5, gradients elementwise |d| <= 1e-4 + 1e-4 |ref|
-    "f32": dict(loss_rel=1e-5, g_atol=1e-4, g_rtol=1e-4, lse_atol=2e-5),
+    # fp32 inputs: loss relative 1e-5; gradients elementwise |d| <= 1e-4 + 1e-4 |ref|
+    # AND normalised max|d| / max|ref| <= 1e-4.  Under mean reduction the gradients
+    # are far below the 1e-4 absolute floor (config-3 grad_x: max 4e-5), so the
+    # elementwise form alone would pass an all-zero gradient; the normalised form
+    # cannot.
+    "f32": dict(loss_rel=1e-5, g_atol=1e-4, g_rtol=1e-4, g_norm=1e-4, lse_atol=2e-5),
     # bf16 inputs, fp32 accumulation: loss relative 2e-3, gradients max|d| / max|ref| <= 1e-2
     "bf16": dict(loss_rel=2e-3, g_norm=1e-2, lse_atol=2e-4),
 }
@@ -47,10 +51,12 @@ def assert_grad_close(got, ref, dtype, name):
         err = np.abs(got - ref) - (tol["g_atol"] + tol["g_rtol"] * np.abs(ref))
         worst = np.unravel_index(np.argmax(err), err.shape)
         assert err.max() <= 0, f"{name}: |d| {abs(got[worst] - ref[worst]):.3e} at {worst}, ref {ref[worst]:.3e}"
-    else:
-        scale = np.abs(ref).max()
-        d = np.abs(got - ref).max() / max(scale, 1e-30)
-        assert d <= tol["g_norm"], f"{name}: max|d|/max|ref| = {d:.3e}"
+    scale = np.abs(ref).max()
+    if scale == 0:
+        assert np.all(got == 0), f"{name}: reference is all zero, result is not"
+        return
+    d = np.abs(got - ref).max() / scale
+    assert d <= tol["g_norm"], f"{name}: max|d|/max|ref| = {d:.3e} (bar {tol['g_norm']:.0e})"
 
 
 def assert_parity(got, ref_loss, ref_lse, ref_zt, ref_gx, ref_gW, dtype):
@@ -65,3 +71,4 @@ def assert_parity(got, ref_loss, ref_lse, ref_zt, ref_gx, ref_gW, dtype):
         assert_grad_close(got["gx"], ref_gx, dtype, "grad_x")
     if ref_gW is not None:
         assert_grad_close(got["gW"], ref_gW, dtype, "grad_W")
+

@@ -1,15 +1,17 @@
 """Parity at the full benchmark sizes, in the launch configuration bench.py times
-(default workspaces), on outputs the float64 oracle can compute one by one:
+(default workspaces), against the float64 oracle:
 
-* lse and the target logit of sampled tokens, and their grad_x rows (each needs
-  only that token's logits);
-* grad_W rows of sampled vocabulary entries (always including targets) wherever
-  the oracle's own lse for every token is affordable (<= ~9e12 flop);
-* the loss against the oracle's full forward where that is affordable, and
-  otherwise the property loss = reduce(lse - target logit) with the sampled
-  terms matching the oracle;
+* the oracle's full forward (lse and target logit of every token, and the loss:
+  2NHV float64 flop, up to 4e13 at 32768 tokens -- tens of seconds on a
+  16-core host) against the GPU's lse, target logits and loss;
+* grad_x rows of sampled tokens (each needs only that token's logits);
+* grad_W rows of sampled vocabulary entries, always including the targets of
+  sampled tokens and the first and last entry (each needs the oracle's lse of
+  every token, which the full forward gives);
 * at every size, the property sum_v grad_W[v, :] = 0 (every dlogit row sums to 0).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -20,9 +22,8 @@ from tests.gpu_util import TOL, note, to_dev, to_f64
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-FULL_ORACLE_FLOP = 9e12  # full float64 forward on the host: ~10 s at ~1 TFLOP/s
 
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["llama3_4k", "llama2_4k", "llama2_32k", "llama3_8k", "llama3_16k",
                                   "llama3_32k", "qwen3_32k", "gemma3_8k"])
 def test_full_size(gpu, name):
@@ -36,6 +37,7 @@ def test_full_size(gpu, name):
     torch.cuda.synchronize()
     note(f"[full] {name} GPU done")
     tol = TOL[dt]
+    gbar = tol["g_norm"]
 
     # property at any size: every dlogit row sums to zero, so do grad_W's columns.
     # What remains is rounding: D is rounded to bf16 (|dD| <= 2^-9 |D|, and a dlogit
@@ -47,29 +49,34 @@ def test_full_size(gpu, name):
     bound = 2.0 ** -8 / N * xf_abs + 2.0 ** -9 * gW.double().abs().sum(dim=0)
     assert bool((colsum <= 1.5 * bound + 1e-12).all()), f"sum_v grad_W exceeds its rounding bound"
 
-    g = np.random.Generator(np.random.PCG64(1))
-    rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 30, replace=False)]))
     xf, Wf = widen(x, dt), widen(W, dt)
     lse_h, zt_h = to_f64(lse), to_f64(zt)
-    r_lse, r_zt = oracle.forward_rows(xf, Wf, t, rows)
-    np.testing.assert_allclose(lse_h[rows], r_lse, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(r_lse).max()))
-    np.testing.assert_allclose(zt_h[rows], r_zt, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(r_zt).max()))
 
-    # grad_x rows: normalised by the largest |grad_x| of the sampled rows
+    # the oracle's full forward: every token's lse and target logit, and the loss
+    t0 = time.perf_counter()
+    ref_loss, ref_lse, ref_zt = oracle.forward(xf, Wf, t, "mean")
+    note(f"[full] {name} oracle forward {time.perf_counter() - t0:.1f} s")
+    assert abs(loss.item() - ref_loss) <= tol["loss_rel"] * abs(ref_loss), (loss.item(), ref_loss)
+    np.testing.assert_allclose(lse_h, ref_lse, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(ref_lse).max()))
+    np.testing.assert_allclose(zt_h, ref_zt, rtol=0, atol=tol["lse_atol"] * max(1.0, np.abs(ref_zt).max()))
+
+    # grad_x rows of sampled tokens: normalised by the largest |grad_x| of those rows
+    g = np.random.Generator(np.random.PCG64(1))
+    rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 30, replace=False)]))
     r_gx = oracle.grad_x_rows(xf, Wf, t, rows, "mean")
     d = np.abs(to_f64(gx[torch.from_numpy(rows).cuda()]) - r_gx).max() / np.abs(r_gx).max()
-    assert d <= (tol["g_norm"] if dt == "bf16" else 1e-4), f"grad_x rows: {d:.3e}"
+    assert d <= gbar, f"grad_x rows: {d:.3e}"
 
-    # loss: consistency with the per-token terms everywhere ...
-    per = lse_h - zt_h
-    assert abs(loss.item() - per.mean()) <= 1e-6 * abs(per.mean())
-    if 2.0 * N * H * V <= FULL_ORACLE_FLOP:
-        # ... and the oracle's own full forward where affordable
-        ref_loss, ref_lse, _ = oracle.forward(xf, Wf, t, "mean")
-        note(f"[full] {name} oracle forward done")
-        assert abs(loss.item() - ref_loss) <= tol["loss_rel"] * abs(ref_loss)
-        vrows = np.unique(np.concatenate([[0, V - 1], t[rows[:8]], g.choice(V, 24, replace=False)]))
-        r_gW = oracle.grad_w_rows(xf, Wf, t, vrows, ref_lse, "mean")
-        got = to_f64(gW[torch.from_numpy(vrows).cuda()])
-        d = np.abs(got - r_gW).max() / np.abs(r_gW).max()
-        assert d <= (tol["g_norm"] if dt == "bf16" else 1e-4), f"grad_W rows: {d:.3e}"
+    # grad_W rows: targets of sampled tokens (their one-hot terms), the first and
+    # last entry (edge tiles) and random entries, from the oracle's own lse
+    t0 = time.perf_counter()
+    vrows = np.unique(np.concatenate([[0, V - 1], t[rows[:12]], g.choice(V, 20, replace=False)]))
+    r_gW = oracle.grad_w_rows(xf, Wf, t, vrows, ref_lse, "mean")
+    got = to_f64(gW[torch.from_numpy(vrows).cuda()])
+    d = np.abs(got - r_gW).max() / np.abs(r_gW).max()
+    note(f"[full] {name} grad_W rows {time.perf_counter() - t0:.1f} s, err {d:.2e}")
+    assert d <= gbar, f"grad_W rows: {d:.3e}"
+    # the target rows on their own, normalised by their own largest entry
+    tr = np.isin(vrows, t[rows[:12]])
+    d_t = np.abs(got[tr] - r_gW[tr]).max() / np.abs(r_gW[tr]).max()
+    assert d_t <= gbar, f"grad_W target rows: {d_t:.3e}"

@@ -290,3 +290,41 @@ def test_timed_variants_record_every_kernel(gpu):
     bk = [k for k, _ in bt.durations()]
     assert len(bk) % 3 == 0 and bk[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"]
     assert all(ms >= 0 for _, ms in ft.durations() + bt.durations())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_out_of_range_targets(gpu, dtype):
+    """Targets outside [0, V) (a caller error the pages leave open; the library's
+    contract: the token's loss term and target logit are NaN, its dlogit row gets
+    no one-hot term, and nothing is read out of bounds).  Bad targets sit in
+    interior tiles (dlogits' unmasked path) and in the ragged last token tile.
+    Expected values: lse and every other token's outputs are bit-identical to a run
+    with valid targets t0; without the one-hot term a token's dlogit row is
+    s softmax(z_i), so grad_x_i = oracle grad_x_i(t0) + s W[t0_i] and
+    grad_W = oracle grad_W(t0) + sum over bad tokens of s x_i at row t0_i."""
+    N, H, V = 600, 256, 3000
+    note(f"[parity] out-of-range targets {dtype}")
+    x, W, t0 = make_inputs(N, H, V, dtype, seed=41)
+    bad = {5: -1, 100: V, 301: V + 7, 590: -(1 << 40), 599: 1 << 40}
+    t = t0.copy()
+    for i, v in bad.items():
+        t[i] = v
+    good = run_hip(gpu, x, W, t0, dtype, "mean")
+    got = run_hip(gpu, x, W, t, dtype, "mean")
+    idx = np.array(sorted(bad))
+    ok = np.setdiff1d(np.arange(N), idx)
+    assert math.isnan(got["loss"])
+    assert np.all(np.isnan(got["zt"][idx]))
+    assert np.array_equal(got["zt"][ok], good["zt"][ok])
+    assert np.array_equal(got["lse"], good["lse"])
+    assert np.all(np.isfinite(got["gx"])) and np.all(np.isfinite(got["gW"]))
+    assert np.array_equal(got["gx"][ok], good["gx"][ok])
+    xf, Wf = widen(x, dtype), widen(W, dtype)
+    s = 1.0 / N
+    ref_gx = oracle.grad_x_rows(xf, Wf, t0, idx, "mean") + s * Wf[t0[idx]]
+    _, ref_gW = oracle.backward(xf, Wf, t0, "mean")
+    for i in idx:
+        ref_gW[t0[i]] += s * xf[i]
+    from tests.gpu_util import assert_grad_close
+    assert_grad_close(got["gx"][idx], ref_gx, dtype, "grad_x (bad-target rows)")
+    assert_grad_close(got["gW"], ref_gW, dtype, "grad_W")
