@@ -72,7 +72,8 @@ typedef enum {
   FLCE_ERR_ALIAS = 5,     /* an output overlaps an input, another output or ws    */
   FLCE_ERR_ALIGN = 6,     /* misaligned x/W, or H * sizeof(dt) not a multiple of 16 */
   FLCE_ERR_WORKSPACE = 7, /* ws is NULL or smaller than required                  */
-  FLCE_ERR_HIP = 8        /* a HIP launch failed                                  */
+  FLCE_ERR_HIP = 8,       /* a HIP launch failed                                  */
+  FLCE_ERR_SCRATCH = 9    /* sizes beyond flce_forward_noalloc's static scratch    */
 } flce_status;
 
 /* Human-readable name of a status code; never NULL, static storage. */
@@ -102,6 +103,28 @@ flce_status flce_forward(const void* x, const void* W, const int64_t* target, in
                          int64_t H, int64_t V, flce_dtype dt, flce_reduction reduction,
                          float* loss, float* lse, float* target_logit, void* ws,
                          size_t ws_bytes, void* hip_stream);
+
+/*
+ * Forward pass without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments and the
+ * same results, bit for bit, as flce_forward without `ws`/`ws_bytes`: the
+ * forward's workspace is a static device array of FLCE_STATIC_SCRATCH_BYTES
+ * inside the library (one per GPU, held until the process ends).  Sizes whose
+ * forward workspace (flce_forward_workspace_bytes) exceeds it are refused with
+ * FLCE_ERR_SCRATCH before anything is enqueued; for every V, N up to
+ * flce_forward_noalloc_max_tokens(V) fits (about 460k tokens).  The first call on
+ * a device looks the array's device address up (hipGetSymbolAddress); a failure
+ * there is FLCE_ERR_HIP.  Every call on one GPU shares that GPU's array: calls
+ * whose kernels overlap in time on one GPU (e.g. on different streams without
+ * ordering) race and give undefined results; calls ordered on one stream are safe.
+ * Nothing in the array needs clearing between calls.
+ */
+#define FLCE_STATIC_SCRATCH_BYTES (16u << 20)
+int64_t flce_forward_noalloc_max_tokens(int64_t V);
+flce_status flce_forward_noalloc(const void* x, const void* W, const int64_t* target, int64_t N,
+                                 int64_t H, int64_t V, flce_dtype dt, flce_reduction reduction,
+                                 float* loss, float* lse, float* target_logit, void* hip_stream);
 
 /* Bytes of device workspace flce_backward needs for these sizes (a pure function
  * of its arguments; 0 for invalid arguments): the dlogit panel of its default

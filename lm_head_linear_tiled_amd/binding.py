@@ -132,6 +132,10 @@ def load() -> ctypes.CDLL:
     lib.flce_backward_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
                                           vp, vp, vp, sz, vp, tp]
     lib.flce_backward_chunked.restype = ctypes.c_int
+    lib.flce_forward_noalloc_max_tokens.argtypes = [i64]
+    lib.flce_forward_noalloc_max_tokens.restype = i64
+    lib.flce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, f32p, f32p, f32p, vp]
+    lib.flce_forward_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 

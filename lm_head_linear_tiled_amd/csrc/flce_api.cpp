@@ -283,6 +283,9 @@ const char* flce_status_string(flce_status s) {
     case FLCE_ERR_ALIGN: return "FLCE_ERR_ALIGN: x and W must be 16-byte aligned and H * sizeof(dtype) a multiple of 16";
     case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace missing or too small";
     case FLCE_ERR_HIP: return "FLCE_ERR_HIP: a HIP kernel launch failed";
+    case FLCE_ERR_SCRATCH:
+      return "FLCE_ERR_SCRATCH: these sizes need more forward workspace than the library's static scratch "
+             "(FLCE_STATIC_SCRATCH_BYTES, 16 MiB); use flce_forward with a workspace";
   }
   return "FLCE: unknown status";
 }
@@ -327,6 +330,47 @@ flce_status flce_forward_timed(const void* x, const void* W, const int64_t* targ
   const double scale = reduction == FLCE_MEAN ? 1.0 / (double)N : 1.0;
   flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
   rec.start();
+  hipError_t e = flce::launch_forward((int)dt, p, x, W, target, (int)N, (int)H, (int)V, (float*)(base + p.off_m),
+                                      (float*)(base + p.off_s), zt, lse, (double*)(base + p.off_blk), scale, loss,
+                                      (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int64_t flce_forward_noalloc_max_tokens(int64_t V) {
+  if (V < 1 || V > kMaxDim) return 0;
+  // the workspace grows with N (splits level off at the minimum): largest N that fits
+  int64_t lo = 0, hi = kMaxDim;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (plan_forward(mid, V).total <= (size_t)FLCE_STATIC_SCRATCH_BYTES)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+flce_status flce_forward_noalloc(const void* x, const void* W, const int64_t* target, int64_t N, int64_t H,
+                                 int64_t V, flce_dtype dt, flce_reduction reduction, float* loss, float* lse,
+                                 float* target_logit, void* hip_stream) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (!loss || !lse) return FLCE_ERR_NULL;
+  const FwdPlan p = plan_forward(N, V);
+  const size_t es = esize(dt);
+  const Range in[3] = {{x, (size_t)N * H * es}, {W, (size_t)V * H * es}, {target, 8 * (size_t)N}};
+  const Range out[3] = {{loss, 4}, {lse, 4 * (size_t)N}, {target_logit, 4 * (size_t)N}};
+  if (any_alias(in, 3, out, 3, Range{nullptr, 0})) return FLCE_ERR_ALIAS;
+  if (p.total > (size_t)FLCE_STATIC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;
+  // The static scratch's device address (never its host-side name).  Nothing the
+  // forward keeps there must start at zero: every split partial is written before
+  // it is read, and target logits are written by their one owner or set to NaN.
+  void* sp = nullptr;
+  if (flce::static_scratch(&sp) != hipSuccess) return FLCE_ERR_HIP;
+  char* base = (char*)sp;
+  float* zt = target_logit ? target_logit : (float*)(base + p.off_zt);
+  const double scale = reduction == FLCE_MEAN ? 1.0 / (double)N : 1.0;
+  flce::Recorder rec{nullptr, (hipStream_t)hip_stream, hipSuccess};
   hipError_t e = flce::launch_forward((int)dt, p, x, W, target, (int)N, (int)H, (int)V, (float*)(base + p.off_m),
                                       (float*)(base + p.off_s), zt, lse, (double*)(base + p.off_blk), scale, loss,
                                       (hipStream_t)hip_stream, rec);

@@ -23,6 +23,8 @@
 // The three backward kernels compute transposed tiles (the output's contiguous
 // dimension on the accumulator rows) and write them through the LDS stage their
 // last K slice frees (staged_epilogue), as whole 128-byte lines.
+#include <mutex>
+
 #include "gemm_core.h"
 #include "flce_launch.h"
 
@@ -727,6 +729,34 @@ __global__ __launch_bounds__(256) void bwd_gx_reduce(const float* __restrict__ p
 }
 
 __global__ void fill_scalar(float* p, float v) { p[0] = v; }
+
+// Forward workspace of flce_forward_noalloc, for callers that cannot allocate: a
+// file-scope device array (each GPU holds its own copy, at its own address, until
+// the process ends).  In host code its name is only a stand-in, so kernels get
+// the device address looked up below, never the name.
+static __device__ __align__(256) unsigned char scratch[FLCE_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current (hipGetSymbolAddress) and kept.
+hipError_t static_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (host side)

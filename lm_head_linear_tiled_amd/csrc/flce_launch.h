@@ -69,6 +69,10 @@ hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W
 
 hipError_t launch_fill(float* p, float v, hipStream_t st, Recorder& rec);
 
+// Device address, on the current device, of the library's static forward scratch
+// (FLCE_STATIC_SCRATCH_BYTES), looked up once per device.
+hipError_t static_scratch(void** out);
+
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
                            void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, hipStream_t st,

@@ -7,7 +7,7 @@ import pytest
 from lm_head_linear_tiled_amd import binding
 
 F32, BF16, MEAN, SUM = 0, 1, 0, 1
-OK, NULL, SHAPE, DTYPE, RED, ALIAS, ALIGN, WS, HIPERR = range(9)
+OK, NULL, SHAPE, DTYPE, RED, ALIAS, ALIGN, WS, HIPERR, SCRATCH = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = binding.status_string(code)
         assert s.startswith("FLCE_")
     assert "unknown" in binding.status_string(99)
@@ -205,3 +205,27 @@ def test_row_length_limits(lib):
     assert lib.flce_forward_workspace_bytes(1 << 30, 128, 1 << 17, BF16) == 0
     assert lib.flce_forward_workspace_bytes(1 << 30, 128, (1 << 17) - 256, BF16) > 0
     assert bwd(lib, V=2 * MiB + 1, nws=1 << 40) == SHAPE
+
+
+def test_noalloc_forward_limits_and_rejects(lib):
+    """flce_forward_noalloc checks its arguments like flce_forward and refuses sizes
+    whose forward workspace exceeds the static scratch, before any HIP call."""
+    MiB = 1 << 20
+    for V in (1000, 128256, 262208):
+        nmax = lib.flce_forward_noalloc_max_tokens(V)
+        assert nmax > 400000
+        assert lib.flce_forward_workspace_bytes(nmax, 128, V, BF16) <= 16 * MiB
+        assert lib.flce_forward_workspace_bytes(nmax + 1, 128, V, BF16) > 16 * MiB
+    assert lib.flce_forward_noalloc_max_tokens(0) == 0
+
+    def na(x=X, W=Wp, t=T, N=64, H=128, V=1000, dt=F32, red=MEAN, loss=LOSS, lse=LSE, zt=ZT):
+        return lib.flce_forward_noalloc(x, W, t, N, H, V, dt, red, loss, lse, zt, None)
+    assert na(x=None) == NULL
+    assert na(lse=None) == NULL
+    assert na(N=0) == SHAPE
+    assert na(dt=2) == DTYPE
+    assert na(red=5) == RED
+    assert na(W=Wp + 4) == ALIGN
+    assert na(lse=X + 64) == ALIAS
+    assert na(N=lib.flce_forward_noalloc_max_tokens(1000) + 1) == SCRATCH
+    assert "static scratch" in binding.status_string(SCRATCH)
