@@ -30,10 +30,15 @@ def parse():
     ap.add_argument("--workload", default="llama3_4k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--backward", choices=["panels", "chunked"], default="panels",
+    ap.add_argument("--backward", choices=["panels", "chunked", "atomic"], default="panels",
                     help="panels: flce_backward (bounded dlogit panels, the default); chunked: "
-                         "flce_backward_chunked, token chunks over the whole vocabulary, for comparison")
+                         "flce_backward_chunked, token chunks over the whole vocabulary; atomic: "
+                         "flce_backward_atomic, float32 atomic accumulation of both gradients (the last two "
+                         "for comparison)")
     ap.add_argument("--chunk-tokens", type=int, default=1024, help="tokens per chunk for --backward chunked")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of libflce.so instead of the package's (a variant built with "
+                         "python -m lm_head_linear_tiled_amd.build --define NAME=VALUE --out PATH)")
     ap.add_argument("--workspace-mb", type=float, default=None,
                     help="backward workspace in MiB instead of the library's default size (the planner then "
                          "uses the largest dlogit panels whose plan fits)")
@@ -143,6 +148,8 @@ def main():
 
     from lm_head_linear_tiled_amd import binding, roofline
     from lm_head_linear_tiled_amd.inputs import WORKLOADS, make_inputs
+    if args.lib:
+        binding.LIB_PATH = os.path.abspath(args.lib)
 
     w = WORKLOADS[args.workload]
     N, H, V, dtype = w.N, w.H, w.V, w.dtype
@@ -162,6 +169,8 @@ def main():
     fws = torch.empty(binding.forward_workspace_bytes(N, H, V, tdt), dtype=torch.uint8, device=dev)
     if args.backward == "chunked":
         nbws = binding.backward_chunked_workspace_bytes(N, H, V, tdt, args.chunk_tokens)
+    elif args.backward == "atomic":
+        nbws = binding.backward_atomic_workspace_bytes(N, H, V, tdt)
     else:
         nbws = binding.backward_workspace_bytes(N, H, V, tdt)
     if args.workspace_mb is not None:
@@ -175,6 +184,8 @@ def main():
         if args.backward == "chunked":
             gx, gW = binding.flce_backward_chunked(xd, Wd, td, lse, gl, red, chunk_tokens=args.chunk_tokens,
                                                    workspace=bws, timer=bt)
+        elif args.backward == "atomic":
+            gx, gW = binding.flce_backward_atomic(xd, Wd, td, lse, gl, red, workspace=bws, timer=bt)
         else:
             gx, gW = binding.flce_backward(xd, Wd, td, lse, gl, red, workspace=bws, timer=bt)
         return loss, gx, gW
@@ -225,6 +236,7 @@ def main():
     fl_kind = {"fwd_partial": roofline.fwd_flops(N, H, V)}
     for k in ("bwd_dlogits", "bwd_grad_w", "bwd_grad_x"):
         fl_kind[k] = roofline.fwd_flops(N, H, V)  # each backward contraction sums to 2NHV over a step
+    fl_kind["bwd_atomic"] = 3 * roofline.fwd_flops(N, H, V)  # the fused atomic kernel does all three
     kernels = {}
     for name, ms in per.items():
         tot = sum(ms) / args.steps
@@ -256,7 +268,8 @@ def main():
         "data": "synthetic (x~N(0,1), W~N(0,1/sqrt(H)), targets uniform, seed 0)",
         "config": {"workload": f"{args.workload}: LM head V={V} H={H} N={N} {dtype} mean, forward+backward",
                    "N": N, "H": H, "V": V, "reduction": red,
-                   "backward": "panels" if args.backward == "panels" else f"chunked {args.chunk_tokens} tokens",
+                   "backward": {"panels": "panels", "atomic": "atomic"}.get(args.backward,
+                                                                             f"chunked {args.chunk_tokens} tokens"),
                    "backward_workspace_bytes": int(nbws)},
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(roofline.fwd_flops(N, H, V) / (fwd_ms * 1e-3) / 1e12, 2),
@@ -267,7 +280,7 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(dom, args.workload),
+                     "traffic": measured_traffic(dom, args.workload) if not args.lib else None,
                      "traffic_scope": "bytes past the L2 (L2 misses, last-level-cache hits included): rocprofv3 "
                                       "FETCH_SIZE and WRITE_SIZE per launch, scaled by what they read for a plain "
                                       "1 GiB device copy",

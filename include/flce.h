@@ -195,7 +195,10 @@ typedef enum {
   FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
   FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel or a pair    */
   FLCE_K_FILL = 6,        /* writes the implicit grad_loss of 1                    */
-  FLCE_K_BWD_GX_REDUCE = 7 /* adds the K-split partial sums of a grad_x launch       */
+  FLCE_K_BWD_GX_REDUCE = 7, /* adds the K-split partial sums of a grad_x launch      */
+  FLCE_K_BWD_ATOMIC = 8,  /* fused dlogit tile + float32 atomic gradient partials  */
+  FLCE_K_ZERO = 9,        /* zeroes a float32 accumulator                          */
+  FLCE_K_CAST = 10        /* float32 accumulator -> bfloat16 output                */
 } flce_kernel;
 
 typedef struct {
@@ -240,6 +243,32 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
                                   int64_t V, flce_dtype dt, flce_reduction reduction,
                                   int64_t chunk_tokens, void* grad_x, void* grad_W, void* ws,
                                   size_t ws_bytes, void* hip_stream, flce_timing* timing);
+
+/*
+ * Backward with float32 atomics, for comparison with flce_backward's bounded
+ * dlogit panels.  Source: helion PR #1268, PR description (the backward
+ * recomputes the logits, and the weight gradient is accumulated with an atomic
+ * add); Liger-Kernel PR #928 thread (the two in-loop atomic adds are discussed as
+ * a possible bottleneck of the fused backward).  One fused kernel walks the
+ * (256-token tile, 256-vocabulary tile) pairs: it recomputes the logit tile,
+ * forms the dlogit tile (kept in a 256 x 256 slot of `ws` per workgroup, never the
+ * N x V matrix), contracts it with the tile's rows of W and x over the hidden
+ * size and adds both gradients' partial sums into float32 buffers with atomic
+ * adds (grad_x and grad_W themselves for float32; buffers in `ws`, then cast to
+ * bfloat16, for bfloat16).  Arguments and results (up to rounding order) as for
+ * flce_backward_timed; not bitwise reproducible (atomic order).
+ *
+ *   ws, ws_bytes  >= flce_backward_atomic_workspace_bytes(N, H, V, dt) (0 for
+ *                 invalid arguments): 256 dlogit tiles of 256 x 256 plus, for
+ *                 bfloat16, float32 [N, H] and [V, H] accumulators
+ *   timing        as for the *_timed variants; may be NULL
+ */
+size_t flce_backward_atomic_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
+flce_status flce_backward_atomic(const void* x, const void* W, const int64_t* target,
+                                 const float* lse, const float* grad_loss, int64_t N, int64_t H,
+                                 int64_t V, flce_dtype dt, flce_reduction reduction, void* grad_x,
+                                 void* grad_W, void* ws, size_t ws_bytes, void* hip_stream,
+                                 flce_timing* timing);
 
 #ifdef __cplusplus
 }

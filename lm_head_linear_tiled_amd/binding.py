@@ -26,7 +26,7 @@ _ESIZE = {F32: 4, BF16: 2}
 _lib = None
 
 KERNEL_NAMES = ["fwd_partial", "fwd_combine", "fwd_loss", "bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "fill",
-                "bwd_gx_reduce"]
+                "bwd_gx_reduce", "bwd_atomic", "zero", "cast"]
 
 
 class Timing(ctypes.Structure):
@@ -132,6 +132,11 @@ def load() -> ctypes.CDLL:
     lib.flce_backward_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
                                           vp, vp, vp, sz, vp, tp]
     lib.flce_backward_chunked.restype = ctypes.c_int
+    lib.flce_backward_atomic_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.flce_backward_atomic_workspace_bytes.restype = sz
+    lib.flce_backward_atomic.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                         vp, vp, vp, sz, vp, tp]
+    lib.flce_backward_atomic.restype = ctypes.c_int
     lib.flce_forward_noalloc_max_tokens.argtypes = [i64]
     lib.flce_forward_noalloc_max_tokens.restype = i64
     lib.flce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, f32p, f32p, f32p, vp]
@@ -254,6 +259,37 @@ def flce_backward_chunked(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor
                                      grad_loss.data_ptr(), N, H, V, dt, _RED[reduction], chunk_tokens,
                                      gx.data_ptr(), gW.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device),
                                      ctypes.byref(timer.t) if timer is not None else None)
+    if code != 0:
+        raise FLCEError(code)
+    return gx, gW
+
+
+def backward_atomic_workspace_bytes(N: int, H: int, V: int, dtype: torch.dtype) -> int:
+    return int(load().flce_backward_atomic_workspace_bytes(N, H, V, _DT[dtype]))
+
+
+def flce_backward_atomic(x: torch.Tensor, W: torch.Tensor, target: torch.Tensor, lse: torch.Tensor,
+                         grad_loss: torch.Tensor, reduction: str = "mean", workspace: torch.Tensor | None = None,
+                         timer: KernelTimer | None = None):
+    """Backward with float32 atomic accumulation of both gradients (one fused kernel
+    per (token tile, vocabulary tile) pair), for comparison with flce_backward.
+    Return (grad_x [N,H], grad_W [V,H])."""
+    _check(x, W, target, reduction)
+    if lse.dtype != torch.float32 or lse.shape != (x.shape[0],) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [N] tensor")
+    grad_loss = grad_loss.reshape(1).to(device=x.device, dtype=torch.float32).contiguous()
+    lib = load()
+    N, H = x.shape
+    V = W.shape[0]
+    dt = _DT[x.dtype]
+    gx = torch.empty_like(x)
+    gW = torch.empty_like(W)
+    nws = lib.flce_backward_atomic_workspace_bytes(N, H, V, dt)
+    ws = workspace if workspace is not None else torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    code = lib.flce_backward_atomic(x.data_ptr(), W.data_ptr(), target.data_ptr(), lse.data_ptr(),
+                                    grad_loss.data_ptr(), N, H, V, dt, _RED[reduction], gx.data_ptr(), gW.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream(x.device),
+                                    ctypes.byref(timer.t) if timer is not None else None)
     if code != 0:
         raise FLCEError(code)
     return gx, gW

@@ -20,19 +20,32 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libflce.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           *[os.path.join(PKG, s) for s in SOURCES], "-o", tmp]
+def build(verbose: bool = False, defines=(), out: str | None = None) -> str:
+    """Compile every source into libflce.so (always recompiles).
+
+    defines: extra NAME=VALUE macros (the tuning knobs the sources declare with
+    #ifndef, e.g. FLCE_PANEL_MB=64); out: where to put the library instead of the
+    package directory (measurement variants)."""
+    lib = os.path.abspath(out) if out else LIB
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(PKG, "csrc"), *[os.path.join(PKG, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libflce.so for gfx950")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="extra macro for a measurement variant (repeatable)")
+    ap.add_argument("--out", default=None, help="output path (default: the package directory)")
+    a = ap.parse_args()
+    print(build(verbose=a.verbose, defines=a.define, out=a.out))

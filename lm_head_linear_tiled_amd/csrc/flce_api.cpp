@@ -451,6 +451,60 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// Workspace of the float32-atomic backward: kAtomicWGs dlogit tiles (one per
+// workgroup of its persistent grid), then for bfloat16 the float32 grad_x [N, H]
+// and grad_W [V, H] accumulators.
+constexpr int kAtomicWGs = 256;
+struct AtomicPlan {
+  size_t off_dtile, off_gx, off_gw, total;
+};
+AtomicPlan plan_backward_atomic(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  AtomicPlan p{};
+  size_t o = 0;
+  p.off_dtile = o;
+  o = align_up(o + esize(dt) * (size_t)kAtomicWGs * kTile * kTile, 256);
+  const bool bf = dt == FLCE_BF16;
+  p.off_gx = o;
+  o = align_up(o + (bf ? sizeof(float) * (size_t)N * H : 0), 256);
+  p.off_gw = o;
+  o = align_up(o + (bf ? sizeof(float) * (size_t)V * H : 0), 256);
+  p.total = o;
+  return p;
+}
+
+size_t flce_backward_atomic_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
+  if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
+  return plan_backward_atomic(N, H, V, dt).total;
+}
+
+flce_status flce_backward_atomic(const void* x, const void* W, const int64_t* target, const float* lse,
+                                 const float* grad_loss, int64_t N, int64_t H, int64_t V, flce_dtype dt,
+                                 flce_reduction reduction, void* grad_x, void* grad_W, void* ws, size_t ws_bytes,
+                                 void* hip_stream, flce_timing* timing) {
+  flce_status st = check_common(x, W, target, N, H, V, dt, reduction);
+  if (st != FLCE_OK) return st;
+  if (!lse || !grad_loss || !grad_x || !grad_W) return FLCE_ERR_NULL;
+  const size_t es = esize(dt);
+  const Range in[5] = {{x, (size_t)N * H * es},
+                       {W, (size_t)V * H * es},
+                       {target, 8 * (size_t)N},
+                       {lse, 4 * (size_t)N},
+                       {grad_loss, 4}};
+  const Range out[2] = {{grad_x, (size_t)N * H * es}, {grad_W, (size_t)V * H * es}};
+  if (any_alias(in, 5, out, 2, Range{ws, ws_bytes})) return FLCE_ERR_ALIAS;
+  const AtomicPlan p = plan_backward_atomic(N, H, V, dt);
+  if (!ws || ws_bytes < p.total) return FLCE_ERR_WORKSPACE;
+  char* base = (char*)ws;
+  const float red_scale = reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f;
+  flce::Recorder rec{timing, (hipStream_t)hip_stream, hipSuccess};
+  rec.start();
+  hipError_t e = flce::launch_backward_atomic(
+      (int)dt, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V, grad_x, grad_W, base + p.off_dtile,
+      (float*)(base + p.off_gx), (float*)(base + p.off_gw), std::min(kAtomicWGs, flce::device_cu_count()),
+      (hipStream_t)hip_stream, rec);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt) {
   if (!dims_ok(N, H, V) || !dtype_ok(dt) || !rows_ok(H, V, dt)) return 0;
   return 256 + std::max(plan_forward(N, V).total,

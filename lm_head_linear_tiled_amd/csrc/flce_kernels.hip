@@ -415,6 +415,105 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
 }
 
 
+// Tile epilogue of a recomputed logit tile: acc holds S^T for vocabulary rows
+// m0.. and tokens n0.. (the layout of TileGemm G); writes
+// D = s (exp(S - lse) - onehot) for those entries into `panel` [token][vocab]
+// (row stride Vbp, token i at row i - i0, vocabulary v at column v - v0),
+// exactly 0 outside i < N, v < V.  PAIRW: G's waves split into copy and store
+// waves (staged_epilogue).
+template <typename T, class G, int PAIRW>
+__device__ __forceinline__ void dlogit_epilogue(typename G::Acc& acc, int m0, int n0, char* spare,
+                                                const int64_t* __restrict__ target, const float* __restrict__ lse,
+                                                float s, int N, int V, int i0, int v0, int Vbp,
+                                                T* __restrict__ panel) {
+  const int l = (int)threadIdx.x & 63;
+  const int wm = G::wave_m(), wn = G::wave_n();
+  const int vw = m0 + wm * G::WM;  // first vocabulary row of this wave
+  const int tw = n0 + wn * G::WN;  // first token of this wave
+  // lse (log2 units) and target of this lane's token in each column block; a
+  // target outside [0, V) gets no one-hot term
+  float lr[G::FN];
+  int tt[G::FN];
+  bool tv[G::FN];
+#pragma unroll
+  for (int j = 0; j < G::FN; ++j) {
+    // unconditional loads (clamped index), all in flight together
+    const int tok = tw + j * 32 + (l & 31);
+    const int tc = tok < N ? tok : N - 1;
+    const int64_t t64 = target[tc];
+    const float lv = lse[tc];
+    tv[j] = tok < N;
+    lr[j] = tv[j] ? lv * kLog2e : 0.f;
+    tt[j] = tv[j] && t64 >= 0 && t64 < V ? (int)t64 : -1;
+  }
+  // src: the wave whose sub-tile (rows from m0 + WM (src / WGN), tokens from
+  // n0 + WN (src % WGN)) the 16 bytes belong to
+  auto out = [&](int src, int n, int m, uint4 v) {
+    const int vs = m0 + (src / G::WGN) * G::WM, ts = n0 + (src % G::WGN) * G::WN;
+    *reinterpret_cast<uint4*>(panel + (int64_t)(ts + n - i0) * Vbp + (vs - v0) + m) = v;
+  };
+  auto out_own = [&](int n, int m, uint4 v) { out((int)threadIdx.x >> 6, n, m, v); };
+  if (m0 + kTile <= V && n0 + kTile <= N) {
+    // interior tile, no masks: s exp2(a log2e - l) = +-exp2(a log2e - (l - log2|s|)),
+    // so each element costs an fma, an exp2 and a sign flip; the one-hot term of
+    // the target element (one per token column, in at most one lane of one wave)
+    // is patched into the staged values afterwards, computed as before:
+    // fma(s, p, -s).  s = 0 gives exp2(-inf) = 0.
+    const float ls = __builtin_amdgcn_logf(__builtin_fabsf(s));
+    const uint32_t sbit = __float_as_uint(s) & 0x80000000u;
+    float lrs[G::FN];
+    int lt[G::FN];
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      lrs[j] = lr[j] - ls;
+      // target row offset within this wave's rows of this lane's half
+      lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
+    }
+    auto val = [&](int i, int j, int g, float* d) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        d[u] = __uint_as_float(
+            __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lrs[j]))) ^ sbit);
+    };
+    auto fix = [&](int j, int tb, auto&& poke) {
+      const int r = lt[j];
+      const bool hit = r >= 0 && r < G::WM && (r & 4) == 0;
+      if (!__any(hit)) return;
+      if (hit) {
+        // acc[i][j][4 g + u] with i = r / 32, g = r / 8 % 4, u = r % 4
+        const int want = (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) a = want == i * 16 + q ? acc[i][j][q] : a;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(a, kLog2e, -lr[j]));
+        poke(tb + (l & 31), r + 4 * (l >> 5), __builtin_fmaf(s, p, -s));
+      }
+    };
+    if constexpr (PAIRW > 0)
+      staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out, fix);
+    else
+      staged_epilogue<T, G::FM, G::FN>(spare, val, out_own, fix);
+  } else {
+    auto val = [&](int i, int j, int g, float* d) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
+        d[u] = 0.f;
+        if (tv[j] && v < V) {
+          const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr[j]);
+          d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
+        }
+      }
+    };
+    if constexpr (PAIRW > 0)
+      staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out);
+    else
+      staged_epilogue<T, G::FM, G::FN>(spare, val, out_own);
+  }
+}
+
 // Sᵀ tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major), as
 // in the forward, so lse and target are read once per token column; the D tile
 // reaches the panel [token][vocabulary] through the staged epilogue.
@@ -431,8 +530,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   static_assert(G::WM == 64 && G::STAGE_BYTES >= G::NWAVES * 8192, "dlogit staging layout");
   constexpr int PAIRW = kSplitDlogits ? G::NWAVES : 0;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
-  const int l = (int)threadIdx.x & 63;
-  const int wm = G::wave_m(), wn = G::wave_n();
   const Operand<T> A{W, H, V, H};
   const Operand<T> B{x, H, N, H};
   const float s = grad_loss[0] * red_scale;
@@ -444,90 +541,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
     return true;
   };
   auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    const int vw = m0 + wm * G::WM;  // first vocabulary row of this wave
-    const int tw = n0 + wn * G::WN;  // first token of this wave
-    // lse (log2 units) and target of this lane's token in each column block; a
-    // target outside [0, V) gets no one-hot term
-    float lr[G::FN];
-    int tt[G::FN];
-    bool tv[G::FN];
-#pragma unroll
-    for (int j = 0; j < G::FN; ++j) {
-      // unconditional loads (clamped index), all in flight together
-      const int tok = tw + j * 32 + (l & 31);
-      const int tc = tok < N ? tok : N - 1;
-      const int64_t t64 = target[tc];
-      const float lv = lse[tc];
-      tv[j] = tok < N;
-      lr[j] = tv[j] ? lv * kLog2e : 0.f;
-      tt[j] = tv[j] && t64 >= 0 && t64 < V ? (int)t64 : -1;
-    }
-    // src: the wave whose sub-tile (rows from m0 + WM (src / WGN), tokens from
-    // n0 + WN (src % WGN)) the 16 bytes belong to
-    auto out = [&](int src, int n, int m, uint4 v) {
-      const int vs = m0 + (src / G::WGN) * G::WM, ts = n0 + (src % G::WGN) * G::WN;
-      *reinterpret_cast<uint4*>(panel + (int64_t)(ts + n - i0) * Vbp + (vs - v0) + m) = v;
-    };
-    auto out_own = [&](int n, int m, uint4 v) { out((int)threadIdx.x >> 6, n, m, v); };
-    if (m0 + kTile <= V && n0 + kTile <= N) {
-      // interior tile, no masks: s exp2(a log2e - l) = +-exp2(a log2e - (l - log2|s|)),
-      // so each element costs an fma, an exp2 and a sign flip; the one-hot term of
-      // the target element (one per token column, in at most one lane of one wave)
-      // is patched into the staged values afterwards, computed as before:
-      // fma(s, p, -s).  s = 0 gives exp2(-inf) = 0.
-      const float ls = __builtin_amdgcn_logf(__builtin_fabsf(s));
-      const uint32_t sbit = __float_as_uint(s) & 0x80000000u;
-      float lrs[G::FN];
-      int lt[G::FN];
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        lrs[j] = lr[j] - ls;
-        // target row offset within this wave's rows of this lane's half
-        lt[j] = tt[j] < 0 ? -1024 : tt[j] - (vw + 4 * (l >> 5));
-      }
-      auto val = [&](int i, int j, int g, float* d) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          d[u] = __uint_as_float(
-              __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * g + u], kLog2e, -lrs[j]))) ^ sbit);
-      };
-      auto fix = [&](int j, int tb, auto&& poke) {
-        const int r = lt[j];
-        const bool hit = r >= 0 && r < G::WM && (r & 4) == 0;
-        if (!__any(hit)) return;
-        if (hit) {
-          // acc[i][j][4 g + u] with i = r / 32, g = r / 8 % 4, u = r % 4
-          const int want = (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
-          float a = 0.f;
-#pragma unroll
-          for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) a = want == i * 16 + q ? acc[i][j][q] : a;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(a, kLog2e, -lr[j]));
-          poke(tb + (l & 31), r + 4 * (l >> 5), __builtin_fmaf(s, p, -s));
-        }
-      };
-      if constexpr (PAIRW > 0)
-        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out, fix);
-      else
-        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own, fix);
-    } else {
-      auto val = [&](int i, int j, int g, float* d) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int v = vw + i * 32 + 8 * g + 4 * (l >> 5) + u;
-              d[u] = 0.f;
-              if (tv[j] && v < V) {
-                const float p = __builtin_amdgcn_exp2f(acc[i][j][4 * g + u] * kLog2e - lr[j]);
-                d[u] = s * (p - (v == tt[j] ? 1.f : 0.f));
-              }
-            }
-          };
-      if constexpr (PAIRW > 0)
-        staged_epilogue<T, G::FM, G::FN, PAIRW>(spare, val, out);
-      else
-        staged_epilogue<T, G::FM, G::FN>(spare, val, out_own);
-    }
+    dlogit_epilogue<T, G, PAIRW>(acc, m0, n0, spare, target, lse, s, N, V, i0, v0, Vbp, panel);
   };
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);
@@ -728,6 +742,160 @@ __global__ __launch_bounds__(256) void bwd_gx_reduce(const float* __restrict__ p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward with float32 atomics (a comparison for the bounded panels; helion PR
+// #1268, PR description: the weight gradient is accumulated with an atomic add)
+// ---------------------------------------------------------------------------
+// Pairs (token tile, vocabulary tile) in launches of up to 256, one pair per
+// workgroup (bwd_atomic): recompute the pair's logit tile S^T = W_tile . x_tile^T
+// (K = H), write its dlogit tile D [256 tokens][256 vocab] into the workgroup's
+// slot of `dtile` (256 slots, one per workgroup of a launch: never the whole
+// dlogit matrix), then contract D with the tile's rows of W and x over the hidden
+// size and add both gradients' partial sums into float32 buffers with atomics:
+//   grad_x[n0 + i, h] += sum_v D[i, v] W[m0 + v, h]   (one tile per 256 of h, K = 256)
+//   grad_W[m0 + v, h] += sum_i D[i, v] x[n0 + i, h]   (one tile per 256 of h, K = 256)
+// Every partial sum reaches the L2 as an atomic: 4 N H V (1/256 + 1/256) bytes
+// over the whole backward.  The result depends on the order in which the
+// atomics land (not bitwise reproducible).  One pair per workgroup, not a
+// persistent loop over pairs: the loop would keep the per-lane addressing of all
+// three contractions live at once and spill.
+
+// One of the two gradient contractions of a pair's D tile (dt), with its
+// float32 atomic epilogue.
+template <typename T, bool WGRAD>
+__device__ __forceinline__ void atomic_grad_phase(const T* __restrict__ x, const T* __restrict__ W, int N, int H,
+                                                  int V, int m0, int n0, const T* __restrict__ dt,
+                                                  float* __restrict__ gx_acc, float* __restrict__ gw_acc, T* lds) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      GX;  // grad_x^T tile: A = W rows as [k = vocab][m = hidden], B = D as [n = token][k = vocab]
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      GW;  // grad_W^T tile: A = x rows as [k = token][m = hidden], B = D as [k = token][n = vocab]
+  const int tiles_h = (H + kTile - 1) / kTile;
+  const int wm = GX::wave_m(), wn = GX::wave_n();
+  auto hnext = [&](int j, int& hm0, int& hn0) {
+    hm0 = j * kTile;
+    hn0 = 0;
+    return j < tiles_h;
+  };
+  // K of every tile, hidden from the optimiser: a known K of 4 slices gets the
+  // slice loop unrolled, and the unrolled copies spill
+  int Kt = kTile;
+  asm volatile("" : "+s"(Kt));
+  // four float32 atomics per 16 staged bytes (whole 256-byte row segments per 16
+  // lanes), as buffer atomics on the tile's 256 output rows (byte offsets within
+  // them fit 32 bits: a row holds at most 8 MiB)
+  auto add4 = [](__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(v.x), r, off + 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(v.y), r, off + 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(v.z), r, off + 8, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(v.w), r, off + 12, 0, 0);
+  };
+  if constexpr (!WGRAD) {
+    // grad_x rows n0.. : tile (hidden m, token n) added at grad_x[n0 + n][m]
+    typename GX::Acc acc;
+    const Operand<T> A{W + (int64_t)m0 * H, H, H, V - m0 < kTile ? V - m0 : kTile};
+    const Operand<T> B{dt, kTile, kTile, kTile};
+    auto add = [&](typename GX::Acc& a, int hm0, int, char* spare) {
+      auto val = [&](int i, int j, int g, float* d) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d[u] = a[i][j][4 * g + u];
+      };
+      const int hw = hm0 + wm * GX::WM, nw = wn * GX::WN;
+      const int rows = N - n0 < kTile ? N - n0 : kTile;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(gx_acc + (int64_t)n0 * H), (short)0, (uint32_t)rows * (uint32_t)H * 4u, 0x00020000);
+      staged_epilogue<float, GX::FM, GX::FN>(spare, val, [&](int n, int m, uint4 v) {
+        const int t = nw + n, h = hw + m;
+        if (t < rows && h < H) add4(r, ((uint32_t)t * (uint32_t)H + (uint32_t)h) * 4u, v);
+      });
+    };
+    GX::run_tiles(A, B, Kt, lds, acc, hnext, add);
+  } else {
+    // grad_W rows m0.. : tile (hidden m, vocabulary n) added at grad_W[m0 + n][m]
+    typename GW::Acc acc;
+    const Operand<T> A{x + (int64_t)n0 * H, H, H, N - n0 < kTile ? N - n0 : kTile};
+    const Operand<T> B{dt, kTile, kTile, kTile};
+    auto add = [&](typename GW::Acc& a, int hm0, int, char* spare) {
+      auto val = [&](int i, int j, int g, float* d) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d[u] = a[i][j][4 * g + u];
+      };
+      const int hw = hm0 + wm * GW::WM, nw = wn * GW::WN;
+      const int rows = V - m0 < kTile ? V - m0 : kTile;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(gw_acc + (int64_t)m0 * H), (short)0, (uint32_t)rows * (uint32_t)H * 4u, 0x00020000);
+      staged_epilogue<float, GW::FM, GW::FN>(spare, val, [&](int n, int m, uint4 v) {
+        const int vr = nw + n, h = hw + m;
+        if (vr < rows && h < H) add4(r, ((uint32_t)vr * (uint32_t)H + (uint32_t)h) * 4u, v);
+      });
+    };
+    GW::run_tiles(A, B, Kt, lds, acc, hnext, add);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_atomic(const T* __restrict__ x, const T* __restrict__ W,
+                                                       const int64_t* __restrict__ target,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ grad_loss, float red_scale, int N,
+                                                       int H, int V, int tiles_t, int tiles_v, int pair0,
+                                                       T* __restrict__ dtile, float* __restrict__ gx_acc,
+                                                       float* __restrict__ gw_acc) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_DMA,
+                   kSplitDlogits>
+      GS;  // logit tile, as in bwd_dlogits
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      GX;  // grad_x^T tile: A = W rows as [k = vocab][m = hidden], B = D as [n = token][k = vocab]
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
+      GW;  // grad_W^T tile: A = x rows as [k = token][m = hidden], B = D as [k = token][n = vocab]
+  static_assert(GS::LDS_ELEMS == GX::LDS_ELEMS && GX::LDS_ELEMS == GW::LDS_ELEMS, "one LDS array");
+  constexpr int PAIRW = kSplitDlogits ? GS::NWAVES : 0;
+  __shared__ __attribute__((aligned(16))) T lds[GS::LDS_ELEMS];
+  const int p = pair0 + xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
+  if (p >= tiles_t * tiles_v) return;
+  int tm, tn;  // vocabulary tile, token tile
+  grouped_tile<FLCE_GROUP_M_WIDE>(p, tiles_v, tiles_t, tm, tn);
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  T* const dt = dtile + (int64_t)blockIdx.x * kTile * kTile;
+  const float s = grad_loss[0] * red_scale;
+  {
+    auto one = [&](int j, int& am0, int& an0) {
+      am0 = m0;
+      an0 = n0;
+      return j == 0;
+    };
+    auto store = [&](typename GS::Acc& a, int am0, int an0, char* spare) {
+      dlogit_epilogue<T, GS, PAIRW>(a, am0, an0, spare, target, lse, s, N, V, n0, m0, kTile, dt);
+    };
+    typename GS::Acc acc;
+    GS::run_tiles(Operand<T>{W, H, V, H}, Operand<T>{x, H, N, H}, H, lds, acc, one, store);
+  }
+  // the D tile's stores are complete and visible to the whole workgroup
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  atomic_grad_phase<T, false>(x, W, N, H, V, m0, n0, dt, gx_acc, gw_acc, lds);
+  atomic_grad_phase<T, true>(x, W, N, H, V, m0, n0, dt, gx_acc, gw_acc, lds);
+}
+
+// Zero n floats (a fill kernel rather than a memset, so that the call can be
+// captured in a HIP graph).
+__global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t n4 = n / 4;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (int64_t)gridDim.x * 256)
+    reinterpret_cast<float4*>(p)[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t q = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (int64_t)gridDim.x * 256) p[q] = 0.f;
+}
+
+// float32 -> bfloat16 (round to nearest even) of n values, n a multiple of 4.
+__global__ __launch_bounds__(256) void cast_f32_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst,
+                                                     int64_t n) {
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n / 4; q += (int64_t)gridDim.x * 256) {
+    const float4 a = reinterpret_cast<const float4*>(src)[q];
+    reinterpret_cast<uint2*>(dst)[q] = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+  }
+}
+
 __global__ void fill_scalar(float* p, float v) { p[0] = v; }
 
 // Forward workspace of flce_forward_noalloc, for callers that cannot allocate: a
@@ -861,6 +1029,51 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
   }
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : rec.err;
+}
+
+template <typename T>
+static hipError_t launch_bwd_atomic_t(const void* xv, const void* Wv, const int64_t* target, const float* lse,
+                                      const float* grad_loss, float red_scale, int N, int H, int V, void* gxv,
+                                      void* gwv, void* dtile, float* gx_acc, float* gw_acc, int max_wgs,
+                                      hipStream_t st, Recorder& rec) {
+  const bool f32 = sizeof(T) == 4;
+  float* gxa = f32 ? (float*)gxv : gx_acc;
+  float* gwa = f32 ? (float*)gwv : gw_acc;
+  const int64_t nx = (int64_t)N * H, nw = (int64_t)V * H;
+  auto fill_grid = [&](int64_t n) { return dim3((unsigned)std::min<int64_t>((n / 4 + 255) / 256 + 1, 4096)); };
+  rec.start();
+  hipLaunchKernelGGL(zero_f32, fill_grid(nx), dim3(256), 0, st, gxa, nx);
+  rec.after(FLCE_K_ZERO);
+  hipLaunchKernelGGL(zero_f32, fill_grid(nw), dim3(256), 0, st, gwa, nw);
+  rec.after(FLCE_K_ZERO);
+  const int tiles_t = (N + kTile - 1) / kTile, tiles_v = (V + kTile - 1) / kTile;
+  const int pairs = tiles_t * tiles_v;
+  // launches of max_wgs pairs, one per workgroup, each with its own D tile slot;
+  // stream order keeps a slot from being reused before its last reader is done
+  for (int p0 = 0; p0 < pairs; p0 += max_wgs) {
+    const int grid = std::min(max_wgs, pairs - p0);
+    hipLaunchKernelGGL(bwd_atomic<T>, dim3(grid), dim3(kThreads), 0, st, (const T*)xv, (const T*)Wv, target, lse,
+                       grad_loss, red_scale, N, H, V, tiles_t, tiles_v, p0, (T*)dtile, gxa, gwa);
+    rec.after(FLCE_K_BWD_ATOMIC);
+  }
+  if (!f32) {
+    hipLaunchKernelGGL(cast_f32_bf16, fill_grid(nx), dim3(256), 0, st, (const float*)gxa, (bf16_t*)gxv, nx);
+    rec.after(FLCE_K_CAST);
+    hipLaunchKernelGGL(cast_f32_bf16, fill_grid(nw), dim3(256), 0, st, (const float*)gwa, (bf16_t*)gwv, nw);
+    rec.after(FLCE_K_CAST);
+  }
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : rec.err;
+}
+
+hipError_t launch_backward_atomic(int dt, const void* x, const void* W, const int64_t* target, const float* lse,
+                                  const float* grad_loss, float red_scale, int N, int H, int V, void* gx, void* gw,
+                                  void* dtile, float* gx_acc, float* gw_acc, int max_wgs, hipStream_t st,
+                                  Recorder& rec) {
+  return dt == 1 ? launch_bwd_atomic_t<bf16_t>(x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, dtile,
+                                               gx_acc, gw_acc, max_wgs, st, rec)
+                 : launch_bwd_atomic_t<float>(x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, dtile,
+                                              gx_acc, gw_acc, max_wgs, st, rec);
 }
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,

@@ -69,6 +69,14 @@ hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W
 
 hipError_t launch_fill(float* p, float v, hipStream_t st, Recorder& rec);
 
+// Float32-atomic backward (comparison): zero the float32 accumulators (grad_x and
+// grad_W themselves for float32), one persistent launch over the (token tile,
+// vocabulary tile) pairs, then casts to bfloat16.  dtile: max_wgs 256 x 256 tiles.
+hipError_t launch_backward_atomic(int dt, const void* x, const void* W, const int64_t* target, const float* lse,
+                                  const float* grad_loss, float red_scale, int N, int H, int V, void* gx, void* gw,
+                                  void* dtile, float* gx_acc, float* gw_acc, int max_wgs, hipStream_t st,
+                                  Recorder& rec);
+
 // Device address, on the current device, of the library's static forward scratch
 // (FLCE_STATIC_SCRATCH_BYTES), looked up once per device.
 hipError_t static_scratch(void** out);

@@ -20,5 +20,7 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.fail("gpu-marked test run without a visible GPU (deselect with -m 'not gpu')")
     from lm_head_linear_tiled_amd import binding
+    if os.environ.get("FLCE_LIB"):  # a measurement variant of the library (same sources, other build macros)
+        binding.LIB_PATH = os.path.abspath(os.environ["FLCE_LIB"])
     binding.load()  # raises if libflce.so is missing
     return binding

@@ -229,3 +229,28 @@ def test_noalloc_forward_limits_and_rejects(lib):
     assert na(lse=X + 64) == ALIAS
     assert na(N=lib.flce_forward_noalloc_max_tokens(1000) + 1) == SCRATCH
     assert "static scratch" in binding.status_string(SCRATCH)
+
+
+def test_backward_atomic_workspace_and_rejects(lib):
+    """flce_backward_atomic: 256 dlogit tiles of 256 x 256, plus float32 [N, H] and
+    [V, H] accumulators for bfloat16 (float32 accumulates in place); argument checks
+    before any HIP call."""
+    N, H, V = 4096, 4096, 128256
+    assert lib.flce_backward_atomic_workspace_bytes(N, H, V, BF16) == 256 * 256 * 256 * 2 + 4 * N * H + 4 * V * H
+    assert lib.flce_backward_atomic_workspace_bytes(N, H, V, F32) == 256 * 256 * 256 * 4
+    assert lib.flce_backward_atomic_workspace_bytes(0, H, V, F32) == 0
+
+    def ba(x=X, W=Wp, t=T, lse=LSE, gl=GL, N=64, H=128, V=1000, dt=F32, red=MEAN, gx=GX, gw=GW, ws=WSP, nws=None):
+        if nws is None:
+            nws = lib.flce_backward_atomic_workspace_bytes(N, H, V, dt) if min(N, H, V) > 0 else 0
+        return lib.flce_backward_atomic(x, W, t, lse, gl, N, H, V, dt, red, gx, gw, ws, nws, None, None)
+    assert ba(lse=None) == NULL
+    assert ba(gw=None) == NULL
+    assert ba(N=0) == SHAPE
+    assert ba(dt=3) == DTYPE
+    assert ba(red=9) == RED
+    assert ba(x=X + 4) == ALIGN
+    assert ba(gx=Wp) == ALIAS
+    assert ba(ws=GX + 16) == ALIAS
+    assert ba(ws=None) == WS
+    assert ba(nws=lib.flce_backward_atomic_workspace_bytes(64, 128, 1000, F32) - 1) == WS

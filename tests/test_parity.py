@@ -19,6 +19,11 @@ def oracle_all(x, W, t, dtype, reduction, grad_loss=1.0):
     return loss, lse, zt, gx, gW
 
 
+def contractions(timer):
+    """The kernel sequence of a timed call."""
+    return [k for k, _ in timer.durations()]
+
+
 def check_case(gpu, N, H, V, dtype, reduction, seed=0, grad_loss=1.0, t=None, bwd_ws_bytes=None, **kw):
     note(f"[parity] N={N} H={H} V={V} {dtype} {reduction} seed={seed} ws={bwd_ws_bytes}")
     x, W, t0 = make_inputs(N, H, V, dtype, seed=seed, **kw)
@@ -86,7 +91,7 @@ def test_grad_x_split_k(gpu, dtype, reduction):
     bt = gpu.KernelTimer(16)
     gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.9], device="cuda"), reduction, timer=bt)
     torch.cuda.synchronize()
-    assert [k for k, _ in bt.durations()] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "bwd_gx_reduce"]
+    assert contractions(bt) == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "bwd_gx_reduce"]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -136,7 +141,7 @@ def test_grad_x_over_panel_pairs(gpu, dtype):
         seq += ["bwd_dlogits", "bwd_grad_w"]
         if p % 2 == 1 or p == panels - 1:
             seq += ["bwd_grad_x", "bwd_gx_reduce"]
-    assert [k for k, _ in bt.durations()] == seq
+    assert contractions(bt) == seq
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -287,7 +292,7 @@ def test_timed_variants_record_every_kernel(gpu):
     assert torch.equal(l1, l2) and torch.equal(gx1, gx2) and torch.equal(gW1, gW2)
     fk = [k for k, _ in ft.durations()]
     assert fk == ["fwd_partial", "fwd_combine", "fwd_loss"]
-    bk = [k for k, _ in bt.durations()]
+    bk = contractions(bt)
     assert len(bk) % 3 == 0 and bk[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"]
     assert all(ms >= 0 for _, ms in ft.durations() + bt.durations())
 
