@@ -26,7 +26,7 @@ _ESIZE = {F32: 4, BF16: 2}
 _lib = None
 
 KERNEL_NAMES = ["fwd_partial", "fwd_combine", "fwd_loss", "bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "fill",
-                "bwd_gx_reduce", "bwd_atomic", "zero", "cast"]
+                "bwd_gx_reduce", "bwd_atomic", "zero", "cast", "tail_fixup", "tail_pieces"]
 
 
 class Timing(ctypes.Structure):

@@ -107,6 +107,16 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
   constexpr double kUnitsPerGB = 32.0;  // accumulator read-modify-write at ~4 TB/s
   const int64_t th = ceil_div(H, kTile);  // hidden tiles of grad_x / grad_W, and 256-slices of H
   auto rounds = [&](int64_t tiles) { return (double)ceil_div(tiles, cus); };
+  // grad_W (and grad_x without K splits): full rounds of whole tiles, the partial
+  // last round cut along K (kunits 256-wide units per tile) into pieces, plus
+  // their float32 fixup
+  auto gw_cost = [&](int64_t tiles, int64_t kunits) {
+    const int64_t g = std::min<int64_t>(tiles, cus);
+    const flce::TailSplit ts = flce::tail_split(tiles, g, cus);
+    if (ts.kts < 2) return rounds(tiles) * kunits;
+    return (double)(ts.full / g) * kunits + (double)ceil_div(kunits, ts.kts) + kLaunch +
+           (double)ts.tail * (ts.kts + 2) * kTile * kTile * 4 / 1e9 * kUnitsPerGB;
+  };
   // chunk and panel sizes: full ones and the ragged last one
   const int64_t nc_full = N / Nc, nc_last = N % Nc, nv_full = V / Vb, nv_last = V % Vb;
   const int64_t n_chunks = nc_full + (nc_last ? 1 : 0), n_panels = nv_full + (nv_last ? 1 : 0);
@@ -119,7 +129,8 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
       if (cnt_v == 0) continue;
       const int64_t tm = ceil_div(Kc, kTile), tv = ceil_div(Kv, kTile);
       const int64_t ks = gx_splits_for(Nc, Vb, H);
-      double one = rounds(tm * tv) * th + rounds(tv * th) * tm + rounds(tm * th * ks) * ceil_div(tv, ks) + 3 * kLaunch;
+      const double gx = ks > 1 ? rounds(tm * th * ks) * ceil_div(tv, ks) : gw_cost(tm * th, tv);
+      double one = rounds(tm * tv) * th + gw_cost(tv * th, tm) + gx + 3 * kLaunch;
       if (ks > 1) one += kLaunch + (double)(ks + 1) * Kc * H * 4 / 1e9 * kUnitsPerGB;  // partial-sum pass
       t += (double)(cnt_c * cnt_v) * one;
     }
@@ -187,6 +198,21 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   o = align_up(o + p.gw_bytes, 256);
   p.off_gxpart = o;
   o = align_up(o + p.gxpart_bytes, 256);
+  // partial tiles for the split tail of grad_W launches: the most any launch
+  // shape (full or ragged chunk x full or ragged panel) needs on kPlanCUs
+  // workgroups (the launcher splits no more than this holds)
+  p.tail_cap = 0;
+  const int64_t th = ceil_div(H, kTile);
+  auto need = [&](int64_t T) {
+    const flce::TailSplit ts = flce::tail_split(T, std::min<int64_t>(T, kPlanCUs), kPlanCUs);
+    p.tail_cap = std::max(p.tail_cap, ts.tail * ts.kts);
+  };
+  for (int64_t Kv : {Vb, V - (p.n_panels - 1) * Vb}) need(ceil_div(Kv, kTile) * th);  // grad_W
+  if (p.gx_splits == 1)
+    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * th);  // grad_x
+  p.tail_bytes = sizeof(float) * (size_t)p.tail_cap * kTile * kTile;
+  p.off_tail = o;
+  o = align_up(o + p.tail_bytes, 256);
   p.total = o;
   return p;
 }
@@ -411,7 +437,7 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
                                        (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
-                                       (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_tail), (hipStream_t)hip_stream, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -447,7 +473,7 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
                                        (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
-                                       (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_tail), (hipStream_t)hip_stream, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -547,7 +573,7 @@ flce_status flce_forward_backward(const void* x, const void* W, const int64_t* t
     e = flce::launch_backward((int)dt, bp, x, W, target, lse, gl,
                               reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f, (int)N, (int)H, (int)V,
                               grad_x, grad_W, base + bp.off_panel, (float*)(base + bp.off_gx),
-                              (float*)(base + bp.off_gw), (float*)(base + bp.off_gxpart), s, rec);
+                              (float*)(base + bp.off_gw), (float*)(base + bp.off_gxpart), (float*)(base + bp.off_tail), s, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

@@ -273,10 +273,11 @@ __global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block
 // tile (tm, tn) taken in the grouped order, so the copy of a tile's first K slice
 // overlaps the previous tile's last slice and epilogue.
 template <int GM = FLCE_GROUP_M>
-__device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n, int& tm, int& tn,
+                                                int ntiles = -1) {
   const int G = (int)gridDim.x;
   const int t = xcd_grouped_id((int)blockIdx.x, G) + j * G;
-  if (t >= tiles_m * tiles_n) return false;
+  if (t >= (ntiles < 0 ? tiles_m * tiles_n : ntiles)) return false;
   grouped_tile<GM>(t, tiles_m, tiles_n, tm, tn);
   return true;
 }
@@ -610,12 +611,14 @@ __device__ __forceinline__ void grad_init(typename G::Acc& acc, int hw, int nw, 
 // grad_Wᵀ tile of the panel: rows = hidden (A = x rows i0.. as [k = token][m =
 // hidden], MN-major), cols = panel vocabulary (B = the panel as [k = token][n =
 // vocabulary], MN-major); written as grad_W rows v0 + n, hidden contiguous.
-// gw_out and gw_acc point at row v0 of their buffers.
+// gw_out and gw_acc point at row v0 of their buffers.  The launch covers the
+// first `ntiles` tiles of the grouped order (the rest: bwd_grad_pieces).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ panel, int Vbp, int Kc,
                                                        const T* __restrict__ x, int H, int V, int i0, int v0,
-                                                       int Vb, int tiles_h, int tiles_v, T* __restrict__ gw_out,
-                                                       float* __restrict__ gw_acc, int accumulate, int final) {
+                                                       int Vb, int tiles_h, int tiles_v, int ntiles,
+                                                       T* __restrict__ gw_out, float* __restrict__ gw_acc,
+                                                       int accumulate, int final) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
@@ -624,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
   const Operand<T> B{panel, Vbp, Vbp, Kc};
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile(j, tiles_h, tiles_v, tm, tn)) return false;
+    if (!persistent_tile(j, tiles_h, tiles_v, tm, tn, ntiles)) return false;
     m0 = tm * kTile;
     n0 = tn * kTile;
     return true;
@@ -641,6 +644,95 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
   G::run_tiles(A, B, Kc, lds, acc, next, store, init);
 }
 
+// The split tail of a gradient launch (the tiles full .. of its grouped order
+// over tiles_m (hidden) x tiles_n, GM its row grouping): workgroup p computes
+// piece q = p % kts of tail tile full + p / kts, i.e. the tile over K offsets
+// [q Kp, (q + 1) Kp) (past the operands' K extent read as zeros), and writes the
+// float32 partial tile [256 n][256 hidden] to pieces + p 256 256;
+// grad_tail_fixup adds the pieces up.  Operands as in bwd_grad_w (WGRAD) or
+// bwd_grad_x (the panel as a K-major operand in blocks).
+template <typename T, bool WGRAD, int GM>
+__global__ __launch_bounds__(kThreads) void bwd_grad_pieces(const T* __restrict__ panel, int Vbp, int Kgp, int Kc,
+                                                            int Kv, const T* __restrict__ src, int H, int i0, int v0,
+                                                            int Ncp, int tiles_m, int tiles_n, int full, int kts,
+                                                            int Kp, float* __restrict__ pieces) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, WGRAD ? MN_MAJOR : K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M,
+                   FLCE_WAVES_N, STAGE_REG>
+      G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+  const int wm = G::wave_m(), wn = G::wave_n();
+  const int p = (int)blockIdx.x;
+  int tm, tn;
+  grouped_tile<GM>(full + p / kts, tiles_m, tiles_n, tm, tn);
+  const int q = p % kts;
+  // grad_W: A = x rows i0.., B = the panel [k = token][n = vocabulary];
+  // grad_x: A = W rows v0.., B = the panel group [n = token][k = vocabulary]
+  const Operand<T> A = WGRAD ? Operand<T>{src + (int64_t)i0 * H, H, H, Kc} : Operand<T>{src + (int64_t)v0 * H, H, H, Kv};
+  const Operand<T> B = WGRAD ? Operand<T>{panel, Vbp, Vbp, Kc}
+                             : Operand<T>{panel, Vbp, Kc, Kgp, Kgp > Vbp ? Vbp : 0x7fffffff, (int64_t)Ncp * Vbp};
+  auto next = [&](int j, int& m0, int& n0, int& kb) {
+    m0 = tm * kTile;
+    n0 = tn * kTile;
+    kb = q * Kp;
+    return j == 0;
+  };
+  float* const pc = pieces + (int64_t)p * kTile * kTile;
+  auto all_rows = [](int) { return true; };
+  auto piece_off = [](int n) { return (int64_t)n * kTile; };
+  auto store = [&](typename G::Acc& a, int, int, char* spare) {
+    grad_epilogue<T, G>(a, spare, wm * G::WM, wn * G::WN, kTile, 0, (T*)nullptr, pc, all_rows, piece_off);
+  };
+  typename G::Acc acc;
+  G::run_tiles(A, B, Kp, lds, acc, next, store, [](typename G::Acc& a, int, int) { G::zero(a); });
+}
+
+// Sum of the kts float32 pieces of each split tail tile of a gradient launch
+// (bwd_grad_w: GM = FLCE_GROUP_M, rows = vocabulary; bwd_grad_x: GM =
+// FLCE_GROUP_M_WIDE, rows = tokens), in a fixed order, plus the earlier launches'
+// sums (accumulate), into the output rows (final: as T) or their float32
+// accumulator.  Tail tile i is tile full + i of the launch's grouped order over
+// tiles_m (hidden) x tiles_n tiles; its row r lands at output row 256 tn + r,
+// which exists below `rows`.  Block b: tail tile b / 64, rows 4 (b % 64) .. + 3;
+// each thread 4 hidden entries.
+template <typename T, int GM>
+__global__ __launch_bounds__(256) void grad_tail_fixup(const float* __restrict__ pieces, int kts, int full,
+                                                       int tiles_m, int tiles_n, int H, int rows,
+                                                       T* __restrict__ out, float* __restrict__ acc_buf,
+                                                       int accumulate, int final) {
+  const int i = (int)blockIdx.x / 64;
+  const int r = ((int)blockIdx.x % 64) * 4 + (int)threadIdx.x / 64;
+  const int c = ((int)threadIdx.x % 64) * 4;
+  int tm, tn;
+  grouped_tile<GM>(full + i, tiles_m, tiles_n, tm, tn);
+  const int h = tm * kTile + c, v = tn * kTile + r;
+  if (v >= rows || h >= H) return;
+  const float* pc = pieces + (int64_t)i * kts * kTile * kTile + r * kTile + c;
+  float4 a = *reinterpret_cast<const float4*>(pc);
+  for (int q = 1; q < kts; ++q) {
+    const float4 b = *reinterpret_cast<const float4*>(pc + (int64_t)q * kTile * kTile);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  const int64_t o = (int64_t)v * H + h;
+  if (accumulate) {
+    const float4 b = *reinterpret_cast<const float4*>(acc_buf + o);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  if (final) {
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<uint2*>(out + o) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+    else
+      *reinterpret_cast<float4*>(out + o) = a;
+  } else {
+    *reinterpret_cast<float4*>(acc_buf + o) = a;
+  }
+}
+
 // grad_xᵀ tile of the token chunk: rows = hidden (A = W rows v0.. as [k =
 // vocabulary][m = hidden], MN-major), cols = chunk tokens (B = the panel as [n =
 // token][k = vocabulary], K-major; Kgp padded columns, each Vbp of them in a
@@ -648,13 +740,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
 // the panel's vocabulary is split into ks ranges of Ks entries: work item
 // (split s, tile) covers range s and writes its float32 partial sums to
 // part + s * Ncp * H (rows chunk-local); split 0 starts from the sums of earlier
-// panels; bwd_gx_reduce adds the splits.
+// panels; bwd_gx_reduce adds the splits.  The launch covers the first `nitems`
+// work items (without splits, the tiles after them: bwd_grad_pieces).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ panel, int Vbp, int Kgp, int Kc, int Kv,
                                                        const T* __restrict__ W, int H, int N, int i0, int v0,
                                                        int tiles_h, int tiles_t, int ks, int Ks, int Ncp,
                                                        T* __restrict__ gx_out, float* __restrict__ gx_acc,
-                                                       float* __restrict__ part, int accumulate, int final) {
+                                                       float* __restrict__ part, int accumulate, int final,
+                                                       int nitems) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
@@ -668,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   auto item = [&](int j, int& s, int& m0, int& n0) {
     const int G_ = (int)gridDim.x;
     const int t = xcd_grouped_id((int)blockIdx.x, G_) + j * G_;
-    if (t >= tiles * ks) return false;
+    if (t >= nitems) return false;
     s = t / tiles;
     int tm, tn;
     grouped_tile<FLCE_GROUP_M_WIDE>(t - s * tiles, tiles_h, tiles_t, tm, tn);
@@ -964,11 +1058,26 @@ hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W
                                        rec);
 }
 
+// The tail split of one gradient launch (T tiles on G workgroups, KT K slices of
+// BK per tile): tail tiles, pieces per tail tile, K extent per piece (a whole
+// number of slices); tail = 0: no split.
+struct Tail {
+  int tail, kts, Kp;
+};
+static Tail plan_tail(int T, int G, int cap, int KT, int BK) {
+  const TailSplit ts = tail_split(T, G, cap);
+  if (ts.kts < 2) return Tail{0, 0, 0};
+  const int per = (KT + ts.kts - 1) / ts.kts;  // K slices per piece
+  const int kts = (KT + per - 1) / per;
+  if (kts < 2) return Tail{0, 0, 0};
+  return Tail{ts.tail, kts, per * BK};
+}
+
 template <typename T>
 static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv, const int64_t* target,
                                const float* lse, const float* grad_loss, float red_scale, int N, int H, int V,
                                void* gxv, void* gwv, void* panelv, float* gx_acc, float* gw_acc, float* gx_part,
-                               hipStream_t st, Recorder& rec) {
+                               float* tail_buf, hipStream_t st, Recorder& rec) {
   const T* x = (const T*)xv;
   const T* W = (const T*)Wv;
   T* gx = (T*)gxv;
@@ -1003,10 +1112,27 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       rec.after(FLCE_K_BWD_DLOGITS);
       // grad_W rows of this panel accumulate over token chunks.
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
-      hipLaunchKernelGGL(bwd_grad_w<T>, grid(tiles_n * tiles_h), dim3(kThreads), 0, st, (const T*)sub, Vbp, Kc, x,
-                         H, V, i0, v0, Kv, tiles_h, tiles_n, gw + (int64_t)v0 * H, gwa, c > 0 ? 1 : 0,
-                         c == p.n_chunks - 1 ? 1 : 0);
-      rec.after(FLCE_K_BWD_GRAD_W);
+      {
+        // the partial last round of tiles is cut along K (tokens) into pieces
+        constexpr int BK = Cfg<T>::BK;
+        const int T_ = tiles_n * tiles_h;
+        const dim3 g = grid(T_);
+        const Tail tl = plan_tail(T_, g.x, p.tail_cap, (Kc + BK - 1) / BK, BK);
+        const int acc_w = c > 0 ? 1 : 0, fin_w = c == p.n_chunks - 1 ? 1 : 0;
+        hipLaunchKernelGGL(bwd_grad_w<T>, g, dim3(kThreads), 0, st, (const T*)sub, Vbp, Kc, x, H, V, i0, v0, Kv,
+                           tiles_h, tiles_n, T_ - tl.tail, gw + (int64_t)v0 * H, gwa, acc_w, fin_w);
+        rec.after(FLCE_K_BWD_GRAD_W);
+        if (tl.tail) {
+          hipLaunchKernelGGL((bwd_grad_pieces<T, true, FLCE_GROUP_M>), dim3(tl.tail * tl.kts), dim3(kThreads), 0, st,
+                             (const T*)sub, Vbp, 0, Kc, 0, x, H, i0, v0, 0, tiles_h, tiles_n, T_ - tl.tail, tl.kts,
+                             tl.Kp, tail_buf);
+          rec.after(FLCE_K_TAIL_PIECES);
+          hipLaunchKernelGGL((grad_tail_fixup<T, FLCE_GROUP_M>), dim3(tl.tail * 64), dim3(256), 0, st,
+                             (const float*)tail_buf, tl.kts, T_ - tl.tail, tiles_h, tiles_n, H, min(Kv, V - v0),
+                             gw + (int64_t)v0 * H, gwa, acc_w, fin_w);
+          rec.after(FLCE_K_TAIL_FIXUP);
+        }
+      }
       if (!gx_now) continue;
       // grad_x rows of this chunk accumulate over panel groups; a launch with
       // few output tiles splits the group's vocabulary (partial sums in gx_part).
@@ -1014,10 +1140,23 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int Ks = (int)((((int64_t)Kg + p.gx_splits - 1) / p.gx_splits + BK - 1) / BK * BK);
       const int ks = (Kg + Ks - 1) / Ks;
       const int acc_x = gv0 > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
-      hipLaunchKernelGGL(bwd_grad_x<T>, grid(tiles_m * tiles_h * ks), dim3(kThreads), 0, st, (const T*)panel, Vbp,
-                         Kgp, Kc, Kg, W, H, N, i0, gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x,
-                         fin_x);
+      // without K splits, the partial last round of tiles is cut along K instead
+      const int Tx = tiles_m * tiles_h;
+      const dim3 gxg = grid(Tx * ks);
+      const Tail tl = ks == 1 ? plan_tail(Tx, gxg.x, p.tail_cap, Ks / BK, BK) : Tail{0, 0, 0};
+      hipLaunchKernelGGL(bwd_grad_x<T>, gxg, dim3(kThreads), 0, st, (const T*)panel, Vbp, Kgp, Kc, Kg, W, H, N, i0,
+                         gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x, Tx * ks - tl.tail);
       rec.after(FLCE_K_BWD_GRAD_X);
+      if (tl.tail) {
+        hipLaunchKernelGGL((bwd_grad_pieces<T, false, FLCE_GROUP_M_WIDE>), dim3(tl.tail * tl.kts), dim3(kThreads), 0,
+                           st, (const T*)panel, Vbp, Kgp, Kc, Kg, W, H, i0, gv0, p.Ncp, tiles_h, tiles_m,
+                           Tx - tl.tail, tl.kts, tl.Kp, tail_buf);
+        rec.after(FLCE_K_TAIL_PIECES);
+        hipLaunchKernelGGL((grad_tail_fixup<T, FLCE_GROUP_M_WIDE>), dim3(tl.tail * 64), dim3(256), 0, st,
+                           (const float*)tail_buf, tl.kts, Tx - tl.tail, tiles_h, tiles_m, H, min(Kc, N - i0),
+                           gx + (int64_t)i0 * H, gxa + (int64_t)i0 * H, acc_x, fin_x);
+        rec.after(FLCE_K_TAIL_FIXUP);
+      }
       if (ks > 1) {
         const int64_t n4 = (int64_t)Kc * H / 4;
         const int rgrid = (int)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)p.max_workgroups);
@@ -1078,12 +1217,12 @@ hipError_t launch_backward_atomic(int dt, const void* x, const void* W, const in
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
-                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, hipStream_t st,
-                           Recorder& rec) {
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, float* tail,
+                           hipStream_t st, Recorder& rec) {
   return dt == 1 ? launch_bwd_t<bf16_t>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                        gw_acc, gx_part, st, rec)
+                                        gw_acc, gx_part, tail, st, rec)
                  : launch_bwd_t<float>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                       gw_acc, gx_part, st, rec);
+                                       gw_acc, gx_part, tail, st, rec);
 }
 
 }  // namespace flce

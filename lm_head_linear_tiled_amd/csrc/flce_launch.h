@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "flce.h"
@@ -26,8 +28,9 @@ struct BwdPlan {
   int gx_group;             // panels kept in the panel buffer (one [Ncp, Vbp] block each); grad_x runs once per group
   int Ncp;                  // Nc padded to kTile
   int gx_splits;            // grad_x K splits per launch (1: none), partial sums in gxpart
-  size_t off_panel, off_gx, off_gw, off_gxpart, total;  // workspace carving (bytes); 0-sized parts unused
-  size_t gx_bytes, gw_bytes, gxpart_bytes;
+  int tail_cap;             // float32 256 x 256 partial tiles for split tail tiles of grad_W launches
+  size_t off_panel, off_gx, off_gw, off_gxpart, off_tail, total;  // workspace carving (bytes); 0-sized parts unused
+  size_t gx_bytes, gw_bytes, gxpart_bytes, tail_bytes;
   int max_workgroups;                       // persistent grid size: one workgroup per CU
 };
 
@@ -83,7 +86,28 @@ hipError_t static_scratch(void** out);
 
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
-                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, hipStream_t st,
-                           Recorder& rec);
+                           void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, float* tail,
+                           hipStream_t st, Recorder& rec);
+
+// Split of the last, partial round of a persistent launch of T tiles on G
+// workgroups: the T - T % G tiles of the full rounds are done whole; the tail
+// (T % G tiles) is cut along K into kts pieces each when at least two pieces per
+// tail tile fit in the G workgroups and in `cap` partial-tile buffers (kts = 0:
+// no split).  Shared by the planner (workspace size) and the launcher.
+struct TailSplit {
+  int full, tail, kts;
+};
+inline TailSplit tail_split(int64_t T, int64_t G, int cap) {
+  TailSplit s{(int)T, 0, 0};
+  if (G <= 0 || T <= 0) return s;
+  const int64_t tail = T % G;
+  if (tail == 0) return s;
+  const int64_t kts = std::min<int64_t>(G, cap) / tail;
+  if (kts < 2) return s;
+  s.full = (int)(T - tail);
+  s.tail = (int)tail;
+  s.kts = (int)kts;
+  return s;
+}
 
 }  // namespace flce

@@ -179,8 +179,11 @@ def test_backward_plan_shapes(lib):
     MB = 1 << 20
     # headline: panels of 4096 tokens x 16384 vocabulary (128 MB bf16), two of them
     # kept at once (all tokens form one chunk: grad_x runs once per pair of panels)
-    # + grad_x accumulator [N, H] f32
-    assert lib.flce_backward_workspace_bytes(4096, 4096, 128256, BF16) == 2 * 128 * MB + 4096 * 4096 * 4
+    # + grad_x accumulator [N, H] f32 + the float32 pieces of the split tail of the
+    # last panel's grad_W launch (53 x 16 = 848 tiles on 256 workgroups: 80 tail
+    # tiles in 3 pieces each)
+    assert lib.flce_backward_workspace_bytes(4096, 4096, 128256, BF16) == \
+        2 * 128 * MB + 4096 * 4096 * 4 + 80 * 3 * 256 * 256 * 4
     # 8192 x 8192 panel (not 32768 x 2048, whose grad_W launches would fill half the CUs)
     # + grad_x accumulator [N, H] + grad_W accumulator [8192, H]
     assert lib.flce_backward_workspace_bytes(32768, 4096, 32000, BF16) == \
