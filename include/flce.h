@@ -199,8 +199,9 @@ typedef enum {
   FLCE_K_BWD_ATOMIC = 8,  /* fused dlogit tile + float32 atomic gradient partials  */
   FLCE_K_ZERO = 9,        /* zeroes a float32 accumulator                          */
   FLCE_K_CAST = 10,       /* float32 accumulator -> bfloat16 output                */
-  FLCE_K_TAIL_FIXUP = 11, /* adds the K pieces of a gradient launch's split tail tiles */
-  FLCE_K_TAIL_PIECES = 12 /* K pieces of the split tail tiles of a gradient launch   */
+  FLCE_K_TAIL_FIXUP = 11, /* adds the K pieces of a launch's split tail tiles (and, for
+                             dlogits, forms the dlogits from the summed logits)     */
+  FLCE_K_TAIL_PIECES = 12 /* K pieces of the split tail tiles of a backward launch   */
 } flce_kernel;
 
 typedef struct {

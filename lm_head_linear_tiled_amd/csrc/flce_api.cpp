@@ -107,9 +107,9 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
   constexpr double kUnitsPerGB = 32.0;  // accumulator read-modify-write at ~4 TB/s
   const int64_t th = ceil_div(H, kTile);  // hidden tiles of grad_x / grad_W, and 256-slices of H
   auto rounds = [&](int64_t tiles) { return (double)ceil_div(tiles, cus); };
-  // grad_W (and grad_x without K splits): full rounds of whole tiles, the partial
-  // last round cut along K (kunits 256-wide units per tile) into pieces, plus
-  // their float32 fixup
+  // dlogits, grad_W (and grad_x without K splits): full rounds of whole tiles,
+  // the partial last round cut along K (kunits 256-wide units per tile) into
+  // pieces, plus their float32 fixup
   auto gw_cost = [&](int64_t tiles, int64_t kunits) {
     const int64_t g = std::min<int64_t>(tiles, cus);
     const flce::TailSplit ts = flce::tail_split(tiles, g, cus);
@@ -130,7 +130,7 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
       const int64_t tm = ceil_div(Kc, kTile), tv = ceil_div(Kv, kTile);
       const int64_t ks = gx_splits_for(Nc, Vb, H);
       const double gx = ks > 1 ? rounds(tm * th * ks) * ceil_div(tv, ks) : gw_cost(tm * th, tv);
-      double one = rounds(tm * tv) * th + gw_cost(tv * th, tm) + gx + 3 * kLaunch;
+      double one = gw_cost(tm * tv, th) + gw_cost(tv * th, tm) + gx + 3 * kLaunch;
       if (ks > 1) one += kLaunch + (double)(ks + 1) * Kc * H * 4 / 1e9 * kUnitsPerGB;  // partial-sum pass
       t += (double)(cnt_c * cnt_v) * one;
     }
@@ -207,7 +207,10 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
     const flce::TailSplit ts = flce::tail_split(T, std::min<int64_t>(T, kPlanCUs), kPlanCUs);
     p.tail_cap = std::max(p.tail_cap, ts.tail * ts.kts);
   };
-  for (int64_t Kv : {Vb, V - (p.n_panels - 1) * Vb}) need(ceil_div(Kv, kTile) * th);  // grad_W
+  for (int64_t Kv : {Vb, V - (p.n_panels - 1) * Vb}) {
+    need(ceil_div(Kv, kTile) * th);  // grad_W
+    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * ceil_div(Kv, kTile));  // dlogits
+  }
   if (p.gx_splits == 1)
     for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * th);  // grad_x
   p.tail_bytes = sizeof(float) * (size_t)p.tail_cap * kTile * kTile;

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
   const int vt_end = min(tiles_v, vt_begin + tiles_per_split);
 
   const int l = (int)threadIdx.x & 63;
-  const int wm = G::wave_m(), wn = G::wave_n();
+  // wave-uniform: kept in scalar registers
+  const int wm = __builtin_amdgcn_readfirstlane(G::wave_m()), wn = __builtin_amdgcn_readfirstlane(G::wave_n());
 
   const Operand<T> A{W, H, V, H};
   const Operand<T> B{x, H, N, H};
@@ -164,11 +165,19 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
         for (int i = 0; i < G::FM; ++i) {
           const int local = local0 - i * 32;
           if (local >= 0 && local < 32 && ((local >> 2) & 1) == (l >> 5)) {
+            // element rr of the lane's 16 accumulators, by a 4-level select tree
+            // on the bits of rr (4 lane masks rather than 16)
             const int rr = (local >> 3) * 4 + (local & 3);
-            float z = 0.f;
+            float v[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z = r == rr ? a[i][j][r] : z;
-            zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = z;
+            for (int r = 0; r < 16; ++r) v[r] = a[i][j][r];
+#pragma unroll
+            for (int b = 0, w = 8; b < 4; ++b, w >>= 1) {
+              const bool hi = (rr >> b) & 1;
+#pragma unroll
+              for (int k = 0; k < w; ++k) v[k] = hi ? v[2 * k + 1] : v[2 * k];
+            }
+            zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = v[0];
           }
         }
       }
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ grad_loss, float red_scale, int N,
                                                         int H, int V, int i0, int v0, int tiles_v, int tiles_t,
-                                                        int Vbp, T* __restrict__ panel) {
+                                                        int ntiles, int Vbp, T* __restrict__ panel) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_DMA,
                    kSplitDlogits>
       G;
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   const float s = grad_loss[0] * red_scale;
   auto next = [&](int j, int& m0, int& n0) {
     int tm, tn;
-    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_v, tiles_t, tm, tn)) return false;
+    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_v, tiles_t, tm, tn, ntiles)) return false;
     m0 = v0 + tm * kTile;
     n0 = i0 + tn * kTile;
     return true;
@@ -546,6 +555,91 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   };
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);
+}
+
+// The split tail of a bwd_dlogits launch (its tiles full .. in the grouped
+// order over tiles_v x tiles_t): workgroup p computes the logit tile S^T of tail
+// tile full + p / kts over hidden offsets [q Kp, (q + 1) Kp), q = p % kts, and
+// writes the float32 partial sums [256 tokens][256 vocabulary] to
+// pieces + p 256 256; dlogit_tail_fixup adds them and forms the dlogits.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_dlogit_pieces(const T* __restrict__ x, const T* __restrict__ W,
+                                                              int N, int H, int V, int i0, int v0, int tiles_v,
+                                                              int tiles_t, int full, int kts, int Kp,
+                                                              float* __restrict__ pieces) {
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_DMA>
+      G;
+  __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
+  const int wm = G::wave_m(), wn = G::wave_n();
+  const int p = (int)blockIdx.x;
+  int tm, tn;
+  grouped_tile<FLCE_GROUP_M_WIDE>(full + p / kts, tiles_v, tiles_t, tm, tn);
+  const int q = p % kts;
+  auto next = [&](int j, int& m0, int& n0, int& kb) {
+    m0 = v0 + tm * kTile;
+    n0 = i0 + tn * kTile;
+    kb = q * Kp;
+    return j == 0;
+  };
+  float* const pc = pieces + (int64_t)p * kTile * kTile;
+  auto all_rows = [](int) { return true; };
+  auto piece_off = [](int n) { return (int64_t)n * kTile; };
+  auto store = [&](typename G::Acc& a, int, int, char* spare) {
+    grad_epilogue<T, G>(a, spare, wm * G::WM, wn * G::WN, kTile, 0, (T*)nullptr, pc, all_rows, piece_off);
+  };
+  typename G::Acc acc;
+  G::run_tiles(Operand<T>{W, H, V, H}, Operand<T>{x, H, N, H}, Kp, lds, acc, next, store,
+               [](typename G::Acc& a, int, int) { G::zero(a); });
+}
+
+// Dlogits of the split tail tiles of a bwd_dlogits launch: S = the sum of the
+// kts pieces (fixed order), then D = s (exp(S - lse) - onehot) for i < N, v < V
+// and 0 elsewhere, into the panel (token i at row i - i0, vocabulary v at column
+// v - v0, row stride Vbp).  Block b: tail tile b / 64, tokens 4 (b % 64) .. + 3
+// of it; each thread 4 vocabulary entries.
+template <typename T>
+__global__ __launch_bounds__(256) void dlogit_tail_fixup(const float* __restrict__ pieces, int kts, int full,
+                                                         int tiles_v, int tiles_t, int N, int V, int i0, int v0,
+                                                         const int64_t* __restrict__ target,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ grad_loss, float red_scale,
+                                                         int Vbp, T* __restrict__ panel) {
+  const int i = (int)blockIdx.x / 64;
+  const int r = ((int)blockIdx.x % 64) * 4 + (int)threadIdx.x / 64;
+  const int c = ((int)threadIdx.x % 64) * 4;
+  int tm, tn;
+  grouped_tile<FLCE_GROUP_M_WIDE>(full + i, tiles_v, tiles_t, tm, tn);
+  const int tok = i0 + tn * kTile + r, vb = v0 + tm * kTile + c;
+  const float* pc = pieces + (int64_t)i * kts * kTile * kTile + r * kTile + c;
+  float4 a = *reinterpret_cast<const float4*>(pc);
+  for (int q = 1; q < kts; ++q) {
+    const float4 b = *reinterpret_cast<const float4*>(pc + (int64_t)q * kTile * kTile);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  const float s = grad_loss[0] * red_scale;
+  float d[4] = {0.f, 0.f, 0.f, 0.f};
+  if (tok < N) {
+    const float lr = lse[tok] * kLog2e;
+    const int64_t t64 = target[tok];
+    const int tt = t64 >= 0 && t64 < V ? (int)t64 : -1;
+    const float sv[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = vb + u;
+      if (v < V) {
+        const float pr = __builtin_amdgcn_exp2f(sv[u] * kLog2e - lr);
+        d[u] = s * (pr - (v == tt ? 1.f : 0.f));
+      }
+    }
+  }
+  T* dst = panel + (int64_t)(tok - i0) * Vbp + (vb - v0);
+  if constexpr (sizeof(T) == 2)
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+  else
+    *reinterpret_cast<float4*>(dst) = make_float4(d[0], d[1], d[2], d[3]);
 }
 
 // Output of a backward contraction through the staged epilogue: out rows are
@@ -1107,9 +1201,25 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int tiles_m = (Kc + kTile - 1) / kTile;
       const int tiles_n = (Kv + kTile - 1) / kTile;
       auto grid = [&](int tiles) { return dim3(min(tiles, p.max_workgroups)); };
-      hipLaunchKernelGGL(bwd_dlogits<T>, grid(tiles_m * tiles_n), dim3(kThreads), 0, st, x, W, target, lse, grad_loss,
-                         red_scale, N, H, V, i0, v0, tiles_n, tiles_m, Vbp, sub);
-      rec.after(FLCE_K_BWD_DLOGITS);
+      {
+        // the partial last round of logit tiles is cut along K (hidden) into pieces
+        constexpr int BK = Cfg<T>::BK;
+        const int T_ = tiles_m * tiles_n;
+        const dim3 g = grid(T_);
+        const Tail tl = plan_tail(T_, g.x, p.tail_cap, (H + BK - 1) / BK, BK);
+        hipLaunchKernelGGL(bwd_dlogits<T>, g, dim3(kThreads), 0, st, x, W, target, lse, grad_loss, red_scale, N, H,
+                           V, i0, v0, tiles_n, tiles_m, T_ - tl.tail, Vbp, sub);
+        rec.after(FLCE_K_BWD_DLOGITS);
+        if (tl.tail) {
+          hipLaunchKernelGGL(bwd_dlogit_pieces<T>, dim3(tl.tail * tl.kts), dim3(kThreads), 0, st, x, W, N, H, V, i0,
+                             v0, tiles_n, tiles_m, T_ - tl.tail, tl.kts, tl.Kp, tail_buf);
+          rec.after(FLCE_K_TAIL_PIECES);
+          hipLaunchKernelGGL(dlogit_tail_fixup<T>, dim3(tl.tail * 64), dim3(256), 0, st, (const float*)tail_buf,
+                             tl.kts, T_ - tl.tail, tiles_n, tiles_m, N, V, i0, v0, target, lse, grad_loss, red_scale,
+                             Vbp, sub);
+          rec.after(FLCE_K_TAIL_FIXUP);
+        }
+      }
       // grad_W rows of this panel accumulate over token chunks.
       float* gwa = f32 ? gwa0 + (int64_t)v0 * H : gwa0;
       {

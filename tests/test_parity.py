@@ -378,3 +378,23 @@ def test_grad_x_tail_split(gpu, dtype, panels):
     assert fixups_after_gx >= 1, seq
     if panels > 1:
         assert seq.count("bwd_grad_x") >= 2, seq
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_dlogits_tail_split(gpu, dtype, reduction):
+    """A dlogit launch of 2 token x 137 vocabulary tiles = 274 tiles on 256
+    workgroups: the 18 tail tiles (vocabulary 32768 ..) are computed as K
+    (hidden) pieces, and the fixup sums them and forms the dlogits, one-hot terms
+    included (several targets sit in the tail tiles, one at V - 1); grad_W's 274
+    tiles split their tail too."""
+    N, H, V = 300, 512, 35000
+    x, W, t = make_inputs(N, H, V, dtype, seed=73)
+    t[:6] = [32768, 33000, 34000, V - 1, 32900, 34999 - 256]
+    got = check_case(gpu, N, H, V, dtype, reduction, seed=73, grad_loss=0.9, t=t)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(32)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.9], device="cuda"), reduction, timer=bt)
+    torch.cuda.synchronize()
+    seq = contractions(bt)
+    assert seq[:6] == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "tail_pieces", "tail_fixup"], seq
