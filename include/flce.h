@@ -189,8 +189,8 @@ flce_status flce_forward_backward(const void* x, const void* W, const int64_t* t
  */
 typedef enum {
   FLCE_K_FWD_PARTIAL = 0, /* logit tiles + online (max, sum-exp) per vocabulary split */
-  FLCE_K_FWD_COMBINE = 1, /* split merge -> lse, per-token loss, block sums          */
-  FLCE_K_FWD_LOSS = 2,    /* block sums -> scalar loss                             */
+  FLCE_K_FWD_COMBINE = 1, /* split merge -> lse, per-token loss, scalar loss         */
+  FLCE_K_FWD_LOSS = 2,    /* (no longer launched: fwd_combine writes the loss)     */
   FLCE_K_BWD_DLOGITS = 3, /* logit tile recompute -> dlogit panel                   */
   FLCE_K_BWD_GRAD_W = 4,  /* grad_W rows of one panel                              */
   FLCE_K_BWD_GRAD_X = 5,  /* grad_x rows of one token chunk, one panel or a pair    */

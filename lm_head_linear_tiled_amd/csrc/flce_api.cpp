@@ -78,8 +78,9 @@ FwdPlan plan_forward(int64_t N, int64_t V) {
   o = align_up(o + sizeof(float) * (size_t)p.splits * p.Np, 256);
   p.off_zt = o;
   o = align_up(o + sizeof(float) * (size_t)p.Np, 256);
+  p.nb = (int)ceil_div(N, 64);
   p.off_blk = o;
-  o = align_up(o + sizeof(double) * (size_t)ceil_div(N, 256), 256);
+  o = align_up(o + sizeof(double) * (size_t)p.nb + sizeof(unsigned int), 256);
   p.total = o;
   return p;
 }

@@ -10,9 +10,9 @@
 //                 that small token counts still fill all 256 CUs (Liger-Kernel PR
 //                 #928 thread: fusing the logits and the softmax leaves too little
 //                 parallelism at small shapes).
-//   fwd_combine   merges the split partials into lse and the per-token loss, then
-//                 reduces the losses per block in a fixed order.
-//   fwd_loss      sums the block partials in a fixed order into the scalar loss.
+//   fwd_combine   merges the split partials into lse and the per-token loss,
+//                 reduces the losses per block in a fixed order, and its last
+//                 block sums the block partials in a fixed order into the loss.
 // Backward (helion PR #1268: the backward recomputes the logits; the dlogits
 // drive both gradients; Liger-Kernel PR #928: zero the out-of-range dlogits):
 //   bwd_dlogits   recomputes a logit tile S^T = W_tile . x_tile^T and writes
@@ -78,11 +78,13 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
                                                    const int64_t* __restrict__ target, int N, int H, int V,
                                                    int tiles_tok, int tiles_per_split, int Np,
                                                    float* __restrict__ part_m, float* __restrict__ part_s,
-                                                   float* __restrict__ zt_out) {
+                                                   float* __restrict__ zt_out, unsigned int* __restrict__ ticket) {
   // S^T tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major).
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
 
+  // the combine kernel's ticket starts from zero (it runs after this kernel)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   const int lid = xcd_grouped_id((int)blockIdx.x, (int)gridDim.x);
   int tt, split;
   grouped_tile(lid, tiles_tok, (int)gridDim.x / tiles_tok, tt, split);
@@ -227,18 +229,31 @@ __global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x,
   }
 }
 
-__global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ part_m,
-                                                   const float* __restrict__ part_s, int splits, int Np, int N,
-                                                   int V, const int64_t* __restrict__ target,
-                                                   float* __restrict__ zt, float* __restrict__ lse,
-                                                   double* __restrict__ block_loss) {
-  __shared__ double red[256];
-  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+// One wavefront per 64 tokens: merge the split partials of each token into lse
+// and its loss term (a NaN target logit for a target outside [0, V)), sum the
+// block's terms in a fixed order; the last block to finish (a ticket counter,
+// zeroed by fwd_partial) sums the block sums in a fixed order into the loss.
+constexpr int kCombineThreads = 64;
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__global__ __launch_bounds__(kCombineThreads) void fwd_combine(const float* __restrict__ part_m,
+                                                               const float* __restrict__ part_s, int splits, int Np,
+                                                               int N, int V, const int64_t* __restrict__ target,
+                                                               float* __restrict__ zt, float* __restrict__ lse,
+                                                               double* __restrict__ block_loss,
+                                                               unsigned int* __restrict__ ticket, double scale,
+                                                               float* __restrict__ loss) {
+  const int i = (int)blockIdx.x * kCombineThreads + (int)threadIdx.x;
   double li = 0.0;
   if (i < N) {
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) M = fmaxf(M, part_m[(int64_t)s * Np + i]);
     float S = 0.f;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) S += part_s[(int64_t)s * Np + i] * exp2f(part_m[(int64_t)s * Np + i] - M);
     const float l2 = M + log2f(S);
     const float lsei = l2 * kLn2;
@@ -251,27 +266,21 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
     }
     li = (double)lsei - (double)z;
   }
-  red[threadIdx.x] = li;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+  li = wave_sum(li);
+  const int nb = (int)gridDim.x;
+  if (threadIdx.x == 0) {
+    block_loss[blockIdx.x] = li;
+    __threadfence();  // the block sum is visible before the ticket is taken
+    const unsigned int k = atomicAdd(ticket, 1u);
+    li = k == (unsigned int)nb - 1 ? 1.0 : 0.0;  // reused as the "last block" flag
   }
-  if (threadIdx.x == 0) block_loss[blockIdx.x] = red[0];
-}
-
-__global__ __launch_bounds__(256) void fwd_loss(const double* __restrict__ block_loss, int nb, double scale,
-                                                float* __restrict__ loss) {
-  __shared__ double red[256];
+  const bool last = __shfl(li, 0) == 1.0 && nb > 0;
+  if (!last) return;
+  __threadfence();  // every other block's sum is visible
   double a = 0.0;
-  for (int b = (int)threadIdx.x; b < nb; b += 256) a += block_loss[b];
-  red[threadIdx.x] = a;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) loss[0] = (float)(red[0] * scale);
+  for (int bb = (int)threadIdx.x; bb < nb; bb += kCombineThreads) a += block_loss[bb];
+  a = wave_sum(a);
+  if (threadIdx.x == 0) loss[0] = (float)(a * scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -1131,14 +1140,11 @@ static hipError_t launch_fwd_t(const FwdPlan& p, const void* x, const void* W, c
   const int grid = p.tiles_tok * p.splits;
   rec.start();
   hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(kThreads), 0, st, (const T*)x, (const T*)W, target, N, H, V,
-                     p.tiles_tok, p.tiles_per_split, p.Np, part_m, part_s, zt);
+                     p.tiles_tok, p.tiles_per_split, p.Np, part_m, part_s, zt, (unsigned int*)(block_loss + p.nb));
   rec.after(FLCE_K_FWD_PARTIAL);
-  const int nb = (N + 255) / 256;
-  hipLaunchKernelGGL(fwd_combine, dim3(nb), dim3(256), 0, st, part_m, part_s, p.splits, p.Np, N, V, target, zt, lse,
-                     block_loss);
+  hipLaunchKernelGGL(fwd_combine, dim3(p.nb), dim3(kCombineThreads), 0, st, part_m, part_s, p.splits, p.Np, N, V,
+                     target, zt, lse, block_loss, (unsigned int*)(block_loss + p.nb), scale, loss);
   rec.after(FLCE_K_FWD_COMBINE);
-  hipLaunchKernelGGL(fwd_loss, dim3(1), dim3(256), 0, st, block_loss, nb, scale, loss);
-  rec.after(FLCE_K_FWD_LOSS);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : rec.err;
 }

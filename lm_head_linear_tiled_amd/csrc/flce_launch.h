@@ -19,7 +19,8 @@ struct FwdPlan {
   int splits;           // vocabulary splits (workgroups per token tile)
   int tiles_per_split;  // vocabulary tiles per split
   int Np;               // tiles_tok * kTile
-  size_t off_m, off_s, off_zt, off_blk, total;  // workspace carving (bytes)
+  int nb;               // combine blocks (64 tokens each)
+  size_t off_m, off_s, off_zt, off_blk, total;  // workspace carving (bytes); off_blk: nb doubles, then a ticket
 };
 
 struct BwdPlan {
