@@ -597,8 +597,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogit_pieces(const T* __restric
     grad_epilogue<T, G>(a, spare, wm * G::WM, wn * G::WN, kTile, 0, (T*)nullptr, pc, all_rows, piece_off);
   };
   typename G::Acc acc;
+  // pieces of whole slices that end at H exactly take the lean copies
   G::run_tiles(Operand<T>{W, H, V, H}, Operand<T>{x, H, N, H}, Kp, lds, acc, next, store,
-               [](typename G::Acc& a, int, int) { G::zero(a); });
+               [](typename G::Acc& a, int, int) { G::zero(a); }, (int64_t)kts * Kp <= H);
 }
 
 // Dlogits of the split tail tiles of a bwd_dlogits launch: S = the sum of the
@@ -786,7 +787,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_pieces(const T* __restrict_
     grad_epilogue<T, G>(a, spare, wm * G::WM, wn * G::WN, kTile, 0, (T*)nullptr, pc, all_rows, piece_off);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Kp, lds, acc, next, store, [](typename G::Acc& a, int, int) { G::zero(a); });
+  // pieces of whole slices that end at the K extent exactly take the lean copies
+  G::run_tiles(A, B, Kp, lds, acc, next, store, [](typename G::Acc& a, int, int) { G::zero(a); },
+               (int64_t)kts * Kp <= (WGRAD ? Kc : Kv));
 }
 
 // Sum of the kts float32 pieces of each split tail tile of a gradient launch
@@ -907,7 +910,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
     };
     G::run_tiles(A, B, Ks, lds, acc, next1, store, init);
   } else {
-    G::run_tiles(A, B, Ks, lds, acc, next, store, init);
+    // splits of whole slices that end at the group's last entry exactly take
+    // the lean copies too
+    G::run_tiles(A, B, Ks, lds, acc, next, store, init, (int64_t)ks * Ks <= Kv);
   }
 }
 

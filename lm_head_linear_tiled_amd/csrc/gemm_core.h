@@ -525,22 +525,26 @@ struct TileGemm {
     }
   }
 
+  // k_whole (split-K sequences, next(j, m0, n0, kb) only): the caller guarantees
+  // that every tile's K range [kb, kb + K) lies inside both operands' K extents
+  // with kb a multiple of BK (so no slice straddles an operand's block split,
+  // itself a multiple of BK), which lets those sequences take the lean copies too.
   template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
-                                                   Next&& next, Epi&& epi, Init&& init) {
+                                                   Next&& next, Epi&& epi, Init&& init, bool k_whole = false) {
     // Lean copies (load_tile, rload) when every slice is a whole K slice -- tiles
-    // start at K offset 0 and K is a multiple of BK inside both K ranges -- and
-    // each operand is either K-major with its K range inside its rows, or (register
-    // staging only) MN-major with every tile inside its mn range.
-    constexpr bool LEAN_OK = (STAGING == STAGE_REG || (AMAJ == K_MAJOR && BMAJ == K_MAJOR)) &&
-                             !std::is_invocable_v<Next&, int, int&, int&, int&>;
+    // start at K offset 0 (or k_whole) and K is a multiple of BK inside both K
+    // ranges -- and each operand is either K-major with its K range inside its
+    // rows, or (register staging only) MN-major with every tile inside its mn range.
+    constexpr bool LEAN_OK = STAGING == STAGE_REG || (AMAJ == K_MAJOR && BMAJ == K_MAJOR);
+    constexpr bool SPLIT_K = std::is_invocable_v<Next&, int, int&, int&, int&>;
     auto fits = [&](const Operand<T>& op, bool kmajor, int MNT) {
       if (op.k_ext < K) return false;
       const int k1 = op.k_ext < op.ksplit ? op.k_ext : op.ksplit;  // K extent of the widest block
       return kmajor ? k1 <= op.ld : op.mn_ext % MNT == 0 && op.mn_ext <= op.ld;
     };
     if constexpr (LEAN_OK) {
-      if (K % BK == 0 && fits(A, AMAJ == K_MAJOR, BM) && fits(B, BMAJ == K_MAJOR, BN)) {
+      if ((!SPLIT_K || k_whole) && K % BK == 0 && fits(A, AMAJ == K_MAJOR, BM) && fits(B, BMAJ == K_MAJOR, BN)) {
         run_tiles_impl<true>(A, B, K, lds, acc, next, epi, init);
         return;
       }
