@@ -56,6 +56,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // stages (one slice in flight while one is multiplied; deeper pipelines measured
 // no faster), and the wave grid of a 256 x 256 tile.
 constexpr int kThreads = 64 * FLCE_WAVES_M * FLCE_WAVES_N;
+// The forward's wave grid on its own (measurement builds: 2 x 2 = one wave per
+// SIMD with a 128 x 128 sub-tile each)
+#ifndef FLCE_FWD_WAVES_M
+#define FLCE_FWD_WAVES_M FLCE_WAVES_M
+#endif
+#ifndef FLCE_FWD_WAVES_N
+#define FLCE_FWD_WAVES_N FLCE_WAVES_N
+#endif
+constexpr int kFwdThreads = 64 * FLCE_FWD_WAVES_M * FLCE_FWD_WAVES_N;
 
 template <typename T>
 struct Cfg;
@@ -74,13 +83,13 @@ struct Cfg<float> {
 // Forward
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void fwd_partial(const T* __restrict__ x, const T* __restrict__ W,
+__global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__ x, const T* __restrict__ W,
                                                    const int64_t* __restrict__ target, int N, int H, int V,
                                                    int tiles_tok, int tiles_per_split, int Np,
                                                    float* __restrict__ part_m, float* __restrict__ part_s,
                                                    float* __restrict__ zt_out, unsigned int* __restrict__ ticket) {
   // S^T tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major).
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_FWD_WAVES_M, FLCE_FWD_WAVES_N> G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
 
   // the combine kernel's ticket starts from zero (it runs after this kernel)
@@ -565,6 +574,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   typename G::Acc acc;
   G::run_tiles(A, B, H, lds, acc, next, store);
 }
+
+// (defined with the gradient kernels below)
+template <typename T, class G, class RowOk, class RowOff>
+__device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare, int hw, int nw, int H, int final,
+                                              T* __restrict__ dst, float* __restrict__ acc_buf, RowOk&& row_ok,
+                                              RowOff&& row_off);
 
 // The split tail of a bwd_dlogits launch (its tiles full .. in the grouped
 // order over tiles_v x tiles_t): workgroup p computes the logit tile S^T of tail
@@ -1144,7 +1159,7 @@ static hipError_t launch_fwd_t(const FwdPlan& p, const void* x, const void* W, c
                                double scale, float* loss, hipStream_t st, Recorder& rec) {
   const int grid = p.tiles_tok * p.splits;
   rec.start();
-  hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(kThreads), 0, st, (const T*)x, (const T*)W, target, N, H, V,
+  hipLaunchKernelGGL(fwd_partial<T>, dim3(grid), dim3(kFwdThreads), 0, st, (const T*)x, (const T*)W, target, N, H, V,
                      p.tiles_tok, p.tiles_per_split, p.Np, part_m, part_s, zt, (unsigned int*)(block_loss + p.nb));
   rec.after(FLCE_K_FWD_PARTIAL);
   hipLaunchKernelGGL(fwd_combine, dim3(p.nb), dim3(kCombineThreads), 0, st, part_m, part_s, p.splits, p.Np, N, V,

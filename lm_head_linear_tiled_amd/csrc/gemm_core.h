@@ -39,6 +39,10 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 enum Major { K_MAJOR = 0, MN_MAJOR = 1 };
 
+#ifndef FLCE_COPY_STEPS
+#define FLCE_COPY_STEPS 0
+#endif
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for_(F&& f) {
@@ -278,9 +282,11 @@ struct TileGemm {
 
   // The copies of one K slice (A's then B's wave instructions, N_VMEM in all) are
   // spread over the first VSTEPS fragment steps, VPER per step, so that the eight
-  // waves do not flood the texture-address queue at the start of a slice.
+  // waves do not flood the texture-address queue at the start of a slice
+  // (FLCE_COPY_STEPS > 0: over that many steps instead, a measurement knob).
   static constexpr int NSTEP_ = BK / KSTEP;
-  static constexpr int VSTEPS = NSTEP_ > 1 ? NSTEP_ - 1 : 1;
+  static constexpr int VSTEPS = FLCE_COPY_STEPS > 0 && FLCE_COPY_STEPS < NSTEP_ ? FLCE_COPY_STEPS
+                                : (NSTEP_ > 1 ? NSTEP_ - 1 : 1);
   static constexpr int VPER = (N_VMEM + VSTEPS - 1) / VSTEPS;
   static constexpr int INSTR_A = BM * BK * ES / 1024 / NCW;
 

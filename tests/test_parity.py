@@ -353,6 +353,26 @@ def test_grad_w_tail_split(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_whole_slice_splits(gpu, dtype):
+    """Split-K work whose K ranges are whole slices ending exactly at the K extent
+    (these take the lean copies): one 36864-entry panel of 144 vocabulary tiles,
+    512 hidden; the dlogit launch's 4 x 144 (bf16: 1024 tokens) or 2 x 144 (fp32:
+    512 tokens) logit tiles leave 64 / 32 tail tiles cut along H into 4 / 8
+    pieces, grad_W's 288 tiles leave 32 cut along the tokens into 8 pieces, and
+    grad_x (8 or 4 output tiles) is split 4 ways over the vocabulary."""
+    N, H, V = (1024 if dtype == "bf16" else 512), 512, 36864
+    got = check_case(gpu, N, H, V, dtype, "mean", seed=74, grad_loss=1.1)
+    x, W, t = make_inputs(N, H, V, dtype, seed=74)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(32)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.1], device="cuda"), "mean", timer=bt)
+    torch.cuda.synchronize()
+    seq = contractions(bt)
+    assert seq == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "tail_pieces", "tail_fixup",
+                   "bwd_grad_x", "bwd_gx_reduce"], seq
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("panels", [1, 3])
 def test_grad_x_tail_split(gpu, dtype, panels):
     """A grad_x launch of 16 token x 17 hidden tiles = 272 tiles on 256
