@@ -93,7 +93,8 @@ size_t flce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype 
  *   target       [N] int64         class index per token, in [0, V)
  *   loss         [1] float32       out: sum or mean of the per-token losses
  *   lse          [N] float32       out: per-token log-sum-exp (input to the backward)
- *   target_logit [N] float32       out, may be NULL: z_{i, t_i} per token
+ *   target_logit [N] float32       out, may be NULL: z_{i, t_i} per token (NaN for a
+ *                                  target outside [0, V))
  *   ws, ws_bytes                   device workspace, >= flce_forward_workspace_bytes
  *
  * The logits are never written to memory.  The result is bitwise reproducible
@@ -113,7 +114,7 @@ flce_status flce_forward(const void* x, const void* W, const int64_t* target, in
  * inside the library (one per GPU, held until the process ends).  Sizes whose
  * forward workspace (flce_forward_workspace_bytes) exceeds it are refused with
  * FLCE_ERR_SCRATCH before anything is enqueued; for every V, N up to
- * flce_forward_noalloc_max_tokens(V) fits (about 460k tokens).  The first call on
+ * flce_forward_noalloc_max_tokens(V) fits (464384 tokens for V > 256).  The first call on
  * a device looks the array's device address up (hipGetSymbolAddress); a failure
  * there is FLCE_ERR_HIP.  Every call on one GPU shares that GPU's array: calls
  * whose kernels overlap in time on one GPU (e.g. on different streams without
@@ -130,8 +131,10 @@ flce_status flce_forward_noalloc(const void* x, const void* W, const int64_t* ta
  * of its arguments; 0 for invalid arguments): the dlogit panel of its default
  * plan (at most 128 MiB, its shape chosen for these sizes), two of them when all
  * tokens form one chunk and the vocabulary takes several panels (grad_x then runs
- * once per pair), plus float32 accumulators where a gradient is summed over
- * several launches.  A smaller workspace, down to
+ * once per pair), float32 accumulators where a gradient is summed over several
+ * launches, and float32 partial tiles for the split tails (the tiles of a
+ * launch's partial last round, cut along K and summed in a fixed order; at most
+ * 256 tiles of 256 KiB).  A smaller workspace, down to
  * flce_backward_min_workspace_bytes, makes the backward keep one panel at a time
  * or use smaller panels (more passes); a larger one changes nothing. */
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
