@@ -45,6 +45,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef FLCE_NSTAGE_F32
 #define FLCE_NSTAGE_F32 2
 #endif
+// MFMA output block of the bfloat16 kernels: 16 (v_mfma_f32_16x16x32_bf16) or 32
+// (v_mfma_f32_32x32x16_bf16); float32 always uses 32 x 32 blocks
+#ifndef FLCE_MI_FWD
+#define FLCE_MI_FWD 32
+#endif
 #ifndef FLCE_WAVES_M
 #define FLCE_WAVES_M 4
 #endif
@@ -72,11 +77,13 @@ template <>
 struct Cfg<bf16_t> {
   static constexpr int BK = FLCE_BK_BF16;
   static constexpr int NS = FLCE_NSTAGE_BF16;
+  static constexpr int MI_FWD = FLCE_MI_FWD;  // MFMA block of the forward
 };
 template <>
 struct Cfg<float> {
   static constexpr int BK = FLCE_BK_F32;
   static constexpr int NS = FLCE_NSTAGE_F32;
+  static constexpr int MI_FWD = 32;
 };
 
 // ---------------------------------------------------------------------------
@@ -89,7 +96,10 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
                                                    float* __restrict__ part_m, float* __restrict__ part_s,
                                                    float* __restrict__ zt_out, unsigned int* __restrict__ ticket) {
   // S^T tile: rows = vocabulary (A = W, K-major), cols = tokens (B = x, K-major).
-  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_FWD_WAVES_M, FLCE_FWD_WAVES_N> G;
+  typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_FWD_WAVES_M, FLCE_FWD_WAVES_N,
+                   STAGE_DMA, false, Cfg<T>::MI_FWD>
+      G;
+  constexpr int MI = G::MI;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
 
   // the combine kernel's ticket starts from zero (it runs after this kernel)
@@ -109,13 +119,14 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
   const Operand<T> A{W, H, V, H};
   const Operand<T> B{x, H, N, H};
 
+  // per column block j: this lane's token n0 + WN wn + MI j + l % MI
   float mrun[G::FN], srun[G::FN];
   int tgt[G::FN];
 #pragma unroll
   for (int j = 0; j < G::FN; ++j) {
     mrun[j] = -INFINITY;
     srun[j] = 0.f;
-    const int tok = n0 + wn * G::WN + j * 32 + (l & 31);
+    const int tok = n0 + wn * G::WN + j * MI + G::acc_n(l);
     tgt[j] = tok < N ? (int)min<int64_t>(max<int64_t>(target[tok], -1), (int64_t)V) : -1;
   }
 
@@ -136,14 +147,14 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, a[i][j][r]);
+          for (int r = 0; r < G::NR; ++r) tmax = fmaxf(tmax, a[i][j][r]);
         tmax *= kLog2e;
       } else {
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+          for (int r = 0; r < G::NR; ++r) {
+            const int v = m0 + wm * G::WM + i * MI + G::acc_m(r, l);
             const float val = v < V ? a[i][j][r] * kLog2e : -INFINITY;
             tmax = fmaxf(tmax, val);
           }
@@ -155,13 +166,13 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
 #pragma unroll
           for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ssum += __builtin_amdgcn_exp2f(__builtin_fmaf(a[i][j][r], kLog2e, -mnew));
+            for (int r = 0; r < G::NR; ++r) ssum += __builtin_amdgcn_exp2f(__builtin_fmaf(a[i][j][r], kLog2e, -mnew));
         } else {
 #pragma unroll
           for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int v = m0 + wm * G::WM + i * 32 + acc_row(r, l);
+            for (int r = 0; r < G::NR; ++r) {
+              const int v = m0 + wm * G::WM + i * MI + G::acc_m(r, l);
               ssum += v < V ? __builtin_amdgcn_exp2f(a[i][j][r] * kLog2e - mnew) : 0.f;
             }
         }
@@ -174,21 +185,23 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
       if (__any(local0 >= 0 && local0 < G::WM)) {
 #pragma unroll
         for (int i = 0; i < G::FM; ++i) {
-          const int local = local0 - i * 32;
-          if (local >= 0 && local < 32 && ((local >> 2) & 1) == (l >> 5)) {
-            // element rr of the lane's 16 accumulators, by a 4-level select tree
-            // on the bits of rr (4 lane masks rather than 16)
-            const int rr = (local >> 3) * 4 + (local & 3);
-            float v[16];
+          const int local = local0 - i * MI;
+          // the lane holding block row `local` of this lane's column, and its register
+          const bool mine = MI == 32 ? ((local >> 2) & 1) == (l >> 5) : (local >> 2) == (l >> 4);
+          if (local >= 0 && local < MI && mine) {
+            const int rr = MI == 32 ? (local >> 3) * 4 + (local & 3) : (local & 3);
+            // element rr of the lane's NR accumulators, by a select tree on the
+            // bits of rr (log2 NR lane masks rather than NR)
+            float v[G::NR];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = a[i][j][r];
+            for (int r = 0; r < G::NR; ++r) v[r] = a[i][j][r];
 #pragma unroll
-            for (int b = 0, w = 8; b < 4; ++b, w >>= 1) {
+            for (int b = 0, w = G::NR / 2; w > 0; ++b, w >>= 1) {
               const bool hi = (rr >> b) & 1;
 #pragma unroll
               for (int k = 0; k < w; ++k) v[k] = hi ? v[2 * k + 1] : v[2 * k];
             }
-            zt_out[n0 + wn * G::WN + j * 32 + (l & 31)] = v[0];
+            zt_out[n0 + wn * G::WN + j * MI + G::acc_n(l)] = v[0];
           }
         }
       }
@@ -196,40 +209,44 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_partial(const T* __restrict__
   };
   G::run_tiles(A, B, H, lds, acc, next, fold);
 
-  // Merge the two lane halves (same token, different vocabulary rows) ...
+  // Merge the lane groups that hold the same tokens (different vocabulary rows)
+  // ...
 #pragma unroll
-  for (int j = 0; j < G::FN; ++j) {
-    const float mo = __shfl_xor(mrun[j], 32);
-    const float so = __shfl_xor(srun[j], 32);
-    const float M = fmaxf(mrun[j], mo);
-    if (M != -INFINITY) {
-      srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - M) + so * __builtin_amdgcn_exp2f(mo - M);
-      mrun[j] = M;
+  for (int sh = MI; sh < 64; sh <<= 1) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const float mo = __shfl_xor(mrun[j], sh);
+      const float so = __shfl_xor(srun[j], sh);
+      const float M = fmaxf(mrun[j], mo);
+      if (M != -INFINITY) {
+        srun[j] = srun[j] * __builtin_amdgcn_exp2f(mrun[j] - M) + so * __builtin_amdgcn_exp2f(mo - M);
+        mrun[j] = M;
+      }
     }
   }
   // ... then the WGM waves that share the token columns, in a fixed order.
   float* sm = reinterpret_cast<float*>(lds);  // [WGM - 1][BN] max, then [WGM - 1][BN] sum
   constexpr int SM = (G::WGM - 1) * kTile;
-  if (wm > 0 && l < 32) {
+  if (wm > 0 && l < MI) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      sm[(wm - 1) * kTile + wn * G::WN + j * 32 + l] = mrun[j];
-      sm[SM + (wm - 1) * kTile + wn * G::WN + j * 32 + l] = srun[j];
+      sm[(wm - 1) * kTile + wn * G::WN + j * MI + l] = mrun[j];
+      sm[SM + (wm - 1) * kTile + wn * G::WN + j * MI + l] = srun[j];
     }
   }
   __syncthreads();
-  if (wm == 0 && l < 32) {
+  if (wm == 0 && l < MI) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
       float M = mrun[j], S = srun[j];
       for (int q = 0; q < G::WGM - 1; ++q) {
-        const float mo = sm[q * kTile + wn * G::WN + j * 32 + l];
-        const float so = sm[SM + q * kTile + wn * G::WN + j * 32 + l];
+        const float mo = sm[q * kTile + wn * G::WN + j * MI + l];
+        const float so = sm[SM + q * kTile + wn * G::WN + j * MI + l];
         const float Mn = fmaxf(M, mo);
         if (Mn != -INFINITY) S = S * __builtin_amdgcn_exp2f(M - Mn) + so * __builtin_amdgcn_exp2f(mo - Mn);
         M = Mn;
       }
-      const int tok = n0 + wn * G::WN + j * 32 + l;
+      const int tok = n0 + wn * G::WN + j * MI + l;
       if (tok < N) {
         part_m[(int64_t)split * Np + tok] = M;
         part_s[(int64_t)split * Np + tok] = S;

@@ -6,16 +6,23 @@
 // K-major ([mn][k], k contiguous, e.g. x [N,H] and W [V,H] contracted over H) or
 // MN-major ([k][mn], mn contiguous, e.g. W [V,H] contracted over V).
 //
-// bfloat16 uses v_mfma_f32_32x32x16_bf16; float32 uses v_mfma_f32_32x32x2f32.
-// Lane layouts (checked on the device):
-//   A operand: lane l holds row m = l % 32, k = KPL * (l / 32) + [0, KPL)
-//   B operand: lane l holds col n = l % 32, k = KPL * (l / 32) + [0, KPL)
-//   C / acc  : lane l, register r holds row 8 (r / 4) + 4 (l / 32) + r % 4, col l % 32
-// with KPL = 8 for bfloat16 and 1 for float32.  MN-major bfloat16 fragments are
-// read with ds_read_b64_tr_b16, which, within each 16-lane group, returns to
-// lane i element j of the 4-element chunk that lane 4 j + i / 4 addressed,
-// position i % 4; pointing lane s at row k0 + s / 4, columns c0 + 4 (s % 4) thus
-// gives lane i the column c0 + i for rows k0 .. k0 + 3.
+// The MFMA shape is a parameter MI: MI x MI output blocks.  MI = 32: bfloat16
+// uses v_mfma_f32_32x32x16_bf16, float32 v_mfma_f32_32x32x2f32; MI = 16
+// (bfloat16 only): v_mfma_f32_16x16x32_bf16.  Lane layouts (checked on the device):
+//   MI = 32:  A operand: lane l holds row m = l % 32, k = KPL * (l / 32) + [0, KPL)
+//             B operand: lane l holds col n = l % 32, k = KPL * (l / 32) + [0, KPL)
+//             C / acc  : lane l, register r holds row 8 (r / 4) + 4 (l / 32) + r % 4, col l % 32
+//             with KPL = 8 for bfloat16 and 1 for float32;
+//   MI = 16:  A operand: lane l holds row m = l % 16, k = 8 (l / 16) + [0, 8)
+//             B operand: lane l holds col n = l % 16, k = 8 (l / 16) + [0, 8)
+//             C / acc  : lane l, register r (of 4) holds row 4 (l / 16) + r, col l % 16.
+// Either way a lane holds runs of four consecutive rows of one column.  At the
+// chip's power limit the 16 x 16 form sustains more bfloat16 MFMA throughput (it
+// moves half the accumulator registers per multiply-add).  MN-major bfloat16
+// fragments are read with ds_read_b64_tr_b16, which, within each 16-lane group,
+// returns to lane i element j of the 4-element chunk that lane 4 j + i / 4
+// addressed, position i % 4; pointing lane s at row k0 + s / 4, columns
+// c0 + 4 (s % 4) thus gives lane i the column c0 + i for rows k0 .. k0 + 3.
 //
 // Out-of-range rows (mn >= mn_ext) and K slices (k >= k_ext) are zero-filled in
 // LDS by the buffer unit's range check, never read from memory.
@@ -33,6 +40,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -113,12 +121,16 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 //   K-major tile  [mn][k], RB-byte rows (RB = BK * sizeof(T), 64 or 128): the
 //       256 / RB rows that share a bank cycle differ in bank half / quarter, and
 //       slot ^ ((row / (256 / RB)) % (RB / 16)) spreads the next rows over slots;
-//   MN-major tile [k][mn], bfloat16 (512-byte rows):  slot ^ (4 (row & 3))
+//   MN-major tile [k][mn], bfloat16 (512-byte rows):  slot ^ (4 (row & 3)) for
+//       MI = 32 (a 32-lane pass reads 4 rows at two column offsets), and
+//       slot ^ (2 (row & 3) + 8 ((row / 8) & 1)) for MI = 16 (a pass reads rows
+//       k .. k + 3 and k + 8 .. k + 11 at one column offset);
 //   MN-major tile [k][mn], float32 (1024-byte rows):  slot ^ (8 (row & 1))
-template <typename T, int MAJ, int RB>
+template <typename T, int MAJ, int RB, int MI = 32>
 __device__ __forceinline__ int swz(int row) {
   if (MAJ == K_MAJOR) return (row / (256 / RB)) % (RB / 16);
-  return sizeof(T) == 2 ? 4 * (row & 3) : 8 * (row & 1);
+  if (sizeof(T) == 4) return 8 * (row & 1);
+  return MI == 16 ? 2 * (row & 3) + 8 * ((row >> 3) & 1) : 4 * (row & 3);
 }
 
 // How a K slice travels from global memory to LDS.
@@ -133,8 +145,10 @@ enum Staging {
 // tile loop -- the memory counter that copies are awaited with also counts
 // stores, in issue order.
 template <typename T, int BM_, int BN_, int BK_, int AMAJ, int BMAJ, int NSTAGE_ = 2, int WGM_ = 2, int WGN_ = 2,
-          int STAGING = STAGE_DMA, bool SPLIT = false>
+          int STAGING = STAGE_DMA, bool SPLIT = false, int MI_ = 32>
 struct TileGemm {
+  static constexpr int MI = MI_;  // MFMA output block: MI x MI
+  static_assert(MI == 32 || (MI == 16 && sizeof(T) == 2), "16 x 16 blocks for bfloat16 only");
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int NSTAGE = NSTAGE_;  // LDS stages: NSTAGE - 1 K slices in flight
   static constexpr int WGM = WGM_, WGN = WGN_;  // wave grid over the tile
@@ -144,10 +158,17 @@ struct TileGemm {
   static_assert(!SPLIT || STAGING == STAGE_DMA, "split copy/store waves need DMA staging");
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VEC = ElemTraits<T>::VEC;
-  static constexpr int KSTEP = ElemTraits<T>::KSTEP;
+  static constexpr int KSTEP = MI == 16 ? 32 : ElemTraits<T>::KSTEP;  // k per MFMA
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static constexpr int FM = WM / MI, FN = WN / MI;
+  static_assert(WM % MI == 0 && WN % MI == 0, "wave tile must be a multiple of the MFMA block");
+  // accumulator registers per block, and the runs of four consecutive rows among them
+  static constexpr int NR = MI * MI / 64, NG = NR / 4;
+  // first row (within its block) of run g of lane l, and the block row / column of
+  // accumulator register r of lane l
+  static __device__ __forceinline__ int qrow(int g, int l) { return MI == 32 ? 8 * g + 4 * (l >> 5) : 4 * (l >> 4); }
+  static __device__ __forceinline__ int acc_m(int r, int l) { return qrow(r >> 2, l) + (r & 3); }
+  static __device__ __forceinline__ int acc_n(int l) { return l & (MI - 1); }
   static_assert(BK * ES == 128 || BK * ES == 64, "K-major rows are 64 or 128 bytes");
 
   static constexpr int A_BYTES = BM * BK * ES;
@@ -164,7 +185,8 @@ struct TileGemm {
   static __device__ __forceinline__ int wave_m() { return ((int)threadIdx.x >> 6) / WGN; }
   static __device__ __forceinline__ int wave_n() { return ((int)threadIdx.x >> 6) % WGN; }
 
-  typedef f32x16_t Acc[FM][FN];
+  typedef std::conditional_t<MI == 32, f32x16_t, f32x4_t> AccT;
+  typedef AccT Acc[FM][FN];
 
   // Row length in bytes of an operand tile stored with major MAJ and mn extent MNT.
   template <int MAJ, int MNT>
@@ -199,7 +221,7 @@ struct TileGemm {
           __builtin_amdgcn_make_buffer_rsrc((void*)(org + (int64_t)mn0 * op.ld), (short)0, num, 0x00020000);
       const int w = (int)threadIdx.x >> 6;
       const int row0 = (J0 * NCW + w) * (64 / SLOTS) + l / SLOTS;
-      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
+      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB, MI>(row0));
       const int ws = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
       for (int j = J0; j < J1; ++j)
@@ -218,7 +240,7 @@ struct TileGemm {
       const int blk = j * NCW + w;  // 1 KiB block of the tile
       const int chunk = blk * 64 + l;
       const int row = chunk / SLOTS;
-      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
+      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB, MI>(row);
       const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
       const int k = MAJ == K_MAJOR ? kg + slot * VEC : kg + row;
       const bool ok = mn < op.mn_ext && k < op.k_ext;
@@ -236,14 +258,14 @@ struct TileGemm {
     const char* sb = (const char*)s;
     const int l = (int)threadIdx.x & 63;
     if (MAJ == K_MAJOR) {
-      const int row = mnb + (l & 31);
-      const int slot = (kk >> 3) + (l >> 5);
-      return *reinterpret_cast<const bf16x8_t*>(sb + row * RB + 16 * (slot ^ swz<bf16_t, MAJ, RB>(row)));
+      const int row = mnb + (l & (MI - 1));
+      const int slot = (kk >> 3) + (MI == 32 ? (l >> 5) : (l >> 4));
+      return *reinterpret_cast<const bf16x8_t*>(sb + row * RB + 16 * (slot ^ swz<bf16_t, MAJ, RB, MI>(row)));
     } else {
       const int g = l >> 4, q = l & 15;
-      const int col = mnb + 16 * (g & 1) + 4 * (q & 3);
-      const int row = kk + 8 * (g >> 1) + (q >> 2);
-      const int cb = 16 * ((col >> 3) ^ swz<bf16_t, MAJ, RB>(row)) + 2 * (col & 7);  // same swizzle for row + 4
+      const int col = MI == 32 ? mnb + 16 * (g & 1) + 4 * (q & 3) : mnb + 4 * (q & 3);
+      const int row = MI == 32 ? kk + 8 * (g >> 1) + (q >> 2) : kk + 8 * g + (q >> 2);
+      const int cb = 16 * ((col >> 3) ^ swz<bf16_t, MAJ, RB, MI>(row)) + 2 * (col & 7);  // same swizzle for row + 4
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + row * RB + cb));
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(sb + (row + 4) * RB + cb));
       const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -259,15 +281,18 @@ struct TileGemm {
     const int l = (int)threadIdx.x & 63;
     if (MAJ == K_MAJOR) {
       const int row = mnb + (l & 31), k = kk + (l >> 5);
-      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((k >> 2) ^ swz<float, MAJ, RB>(row)) + 4 * (k & 3));
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((k >> 2) ^ swz<float, MAJ, RB, MI>(row)) + 4 * (k & 3));
     } else {
       const int row = kk + (l >> 5), col = mnb + (l & 31);
-      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((col >> 2) ^ swz<float, MAJ, RB>(row)) + 4 * (col & 3));
+      return *reinterpret_cast<const float*>(sb + row * RB + 16 * ((col >> 2) ^ swz<float, MAJ, RB, MI>(row)) + 4 * (col & 3));
     }
   }
 
   static __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x16_t mfma(float a, float b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -304,7 +329,7 @@ struct TileGemm {
       // inside the operand.
       constexpr int ROWS_J = NWAVES * 64 / SLOTS;
       static_assert(MAJ == K_MAJOR ? ROWS_J % (256 / RB) == 0 && (ROWS_J / (256 / RB)) % (RB / 16) == 0
-                                   : ROWS_J % (ES == 2 ? 4 : 2) == 0,
+                                   : ROWS_J % (ES == 2 ? (MI == 16 ? 16 : 4) : 2) == 0,
                     "copy j keeps the swizzled slot of copy 0");
       const int l = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
       const uint32_t ldb = (uint32_t)(op.ld * ES);  // at most 8 MiB: offsets stay below 2^31 + 2^23
@@ -325,7 +350,7 @@ struct TileGemm {
         soff = 0;
       }
       const int row0 = (J0 * NWAVES + w) * (64 / SLOTS) + l / SLOTS;
-      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB>(row0));
+      const uint32_t off0 = (uint32_t)row0 * ldb + 16u * (uint32_t)((l % SLOTS) ^ swz<T, MAJ, RB, MI>(row0));
 #pragma unroll
       for (int j = J0; j < J1; ++j)
         r[j - J0] = __builtin_bit_cast(
@@ -342,7 +367,7 @@ struct TileGemm {
       const int blk = j * NWAVES + w;
       const int chunk = blk * 64 + l;
       const int row = chunk / SLOTS;
-      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB>(row);
+      const int slot = (chunk % SLOTS) ^ swz<T, MAJ, RB, MI>(row);
       const int mn = MAJ == K_MAJOR ? mn0 + row : mn0 + slot * VEC;
       const int k = MAJ == K_MAJOR ? kg + slot * VEC : kg + row;
       const bool ok = mn < op.mn_ext && k < op.k_ext;
@@ -432,9 +457,9 @@ struct TileGemm {
   static __device__ __forceinline__ void load_frags(const T* as, const T* bs, int wm, int wn, int kk, FragA (&fa)[FM],
                                                     FragB (&fb)[FN]) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = frag<AMAJ, BM>(as, wm * WM + i * 32, kk);
+    for (int i = 0; i < FM; ++i) fa[i] = frag<AMAJ, BM>(as, wm * WM + i * MI, kk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = frag<BMAJ, BN>(bs, wn * WN + j * 32, kk);
+    for (int j = 0; j < FN; ++j) fb[j] = frag<BMAJ, BN>(bs, wn * WN + j * MI, kk);
   }
 
   // Wait until at most N of this wave's global -> LDS copies are outstanding, then
@@ -456,7 +481,7 @@ struct TileGemm {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
   }
 
   // Multiply one K slice held in LDS stage `cur` into acc while the copy of the
@@ -464,9 +489,58 @@ struct TileGemm {
   // copies are spread over the first fragment steps (DMA) or loaded at the first
   // step and written at the last (register staging), and the LDS fragment reads of
   // step s+1 are interleaved with the MFMAs of step s.
+  // The slice with 16 x 16 blocks (DMA staging): FM x FN = 4 x 8 MFMAs per
+  // fragment step, issued column by column (acc[.][j] for B fragment j), so B
+  // fragment j is dead after its column and the next step's B fragment j is read
+  // into the same registers right after it; only the 4 A fragments are double
+  // buffered (64 fragment registers instead of 96 next to the 128 accumulator
+  // registers).  The instruction order is fixed column by column (a scheduling
+  // barrier after each): the column's MFMAs, then its next-step reads (B j, and
+  // A j for the first FM columns), then its share of the slice's copies (in the
+  // first VSTEPS steps).
+  template <bool LEAN, bool COPY>
+  static __device__ __forceinline__ void slice16(const Operand<T>& A, const Operand<T>& B, T* lds, int cur, int pm0,
+                                                 int pn0, int pk0, Acc& acc) {
+    static_assert(MI == 16 && STAGING == STAGE_DMA, "16 x 16 slice: DMA staging");
+    constexpr int STAGE = STAGE_BYTES / ES;
+    constexpr int AOFF = A_BYTES / ES;
+    constexpr int NSTEP = BK / KSTEP;
+    constexpr int CPC = (VPER + FN - 1) / FN;  // copies per column in a copying step
+    const int wm = wave_m(), wn = wave_n();
+    T* const nstage = lds + (cur ^ 1) * STAGE;
+    const T* as = lds + cur * STAGE;
+    const T* bs = lds + cur * STAGE + AOFF;
+    FragA fa[2][FM];
+    FragB fb[FN];
+    load_frags(as, bs, wm, wn, 0, fa[0], fb);
+    static_for<NSTEP>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      static_for<FN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j] = mfma(fa[s & 1][i], fb[j], acc[i][j]);
+        if constexpr (s + 1 < NSTEP) {
+          fb[j] = frag<BMAJ, BN>(bs, wn * WN + j * MI, (s + 1) * KSTEP);
+          if constexpr (j < FM) fa[(s + 1) & 1][j] = frag<AMAJ, BM>(as, wm * WM + j * MI, (s + 1) * KSTEP);
+        }
+        if constexpr (COPY && s < VSTEPS) {
+          constexpr int c0 = s * VPER + j * CPC, c1 = s * VPER + (j + 1) * CPC;
+          constexpr int e = (s + 1) * VPER < N_VMEM ? (s + 1) * VPER : N_VMEM;
+          constexpr int a0 = c0 < e ? c0 : e, a1 = c1 < e ? c1 : e;
+          if constexpr (a0 < a1) load_part<a0, a1, LEAN>(A, B, pm0, pn0, pk0, nstage);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  }
+
   template <bool LEAN, bool COPY = true>
   static __device__ __forceinline__ void slice(const Operand<T>& A, const Operand<T>& B, T* lds, int cur, int pm0,
                                                int pn0, int pk0, Acc& acc) {
+    if constexpr (MI == 16) {
+      slice16<LEAN, COPY>(A, B, lds, cur, pm0, pn0, pk0, acc);
+      return;
+    }
     constexpr int STAGE = STAGE_BYTES / ES;
     constexpr int AOFF = A_BYTES / ES;
     constexpr int NSTEP = BK / KSTEP;
