@@ -4,10 +4,9 @@
 One step = flce_forward + flce_backward (loss, lse, grad_x, grad_W) over the
 Llama-3 head workload (V=128256, H=4096, N=4096 tokens, bf16 inputs, mean),
 inputs resident in HBM.  Prints one JSON line with the throughput (8NHV flop
-per step, from steps without any instrumentation), forward time, per-kernel
-timings from HIP events recorded between the library's launches in a second pass
-of the same steps, the roofline of the dominant kernel and the CPU oracle timed
-on a bounded sample of the same workload.
+per step), forward time, per-kernel timings from HIP events recorded between
+the library's launches, the roofline of the dominant kernel and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -199,31 +198,17 @@ def main():
     btimers = [binding.KernelTimer(n_bwd_launches + 1) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # the timed steps (the reported value): no instrumentation between the launches
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
     res = None
     for k in range(args.steps):
         res = None  # a step's outputs are dropped before the next step allocates its own
-        res = step()
+        res = step(ftimers[k], btimers[k])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
-
-    # the same steps again with HIP events recorded between the library's launches
-    # on its stream: per-kernel durations and the roofline (each event adds a gap
-    # between two launches, so these steps take a little longer)
-    i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    i0.record()
-    for k in range(args.steps):
-        res = None
-        res = step(ftimers[k], btimers[k])
-    i1.record()
-    torch.cuda.synchronize()
-    ms_step_instrumented = i0.elapsed_time(i1) / args.steps
 
     # forward alone
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -243,7 +228,7 @@ def main():
     peak_mem = torch.cuda.max_memory_allocated()
     res = None
 
-    # per-kernel durations from the events recorded in the instrumented steps; the
+    # per-kernel durations from the events recorded inside the timed steps; the
     # split-tail launches (K pieces and fixup of a launch's partial last round)
     # finish the contraction launched just before them and count towards it
     per = {}
@@ -307,7 +292,6 @@ def main():
         "fwdbwd_frac_of_peak": round(value / peak, 4),
         "fwd_frac_of_peak": round(roofline.fwd_flops(N, H, V) / (fwd_ms * 1e-3) / 1e12 / peak, 4),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "ms_per_step_instrumented": round(ms_step_instrumented, 4),
         "peak_mem_bytes": int(peak_mem),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "avg_launch_ms": round(dom_avg_ms, 4),
