@@ -418,3 +418,64 @@ def test_dlogits_tail_split(gpu, dtype, reduction):
     torch.cuda.synchronize()
     seq = contractions(bt)
     assert seq[:6] == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "tail_pieces", "tail_fixup"], seq
+
+
+def _random_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        dtype = ("f32", "bf16")[k % 2]
+        reduction = ("mean", "sum")[(k // 2) % 2]
+        N = int(rng.integers(1, 700))
+        H = int(8 * rng.integers(1, 129))  # a multiple of 16 bytes in either dtype
+        V = int(rng.integers(1, 5000))
+        gl = float(np.round(rng.uniform(0.5, 2.0), 3))
+        cases.append(pytest.param(N, H, V, dtype, reduction, gl, 100 + k, id=f"{dtype}-{reduction}-{N}x{H}x{V}"))
+    return cases
+
+
+@pytest.mark.parametrize("N,H,V,dtype,reduction,grad_loss,seed", _random_cases())
+def test_random_shapes(gpu, N, H, V, dtype, reduction, grad_loss, seed):
+    """A seeded sweep of small shapes (N in [1, 700), H a multiple of 8 up to 1024, V in
+    [1, 5000)), both dtypes and reductions: ragged tiles on every side, any number of
+    vocabulary splits and panels, split tails where they occur."""
+    check_case(gpu, N, H, V, dtype, reduction, seed=seed, grad_loss=grad_loss)
+
+
+def _random_panel_cases(n=8, seed=2025):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        dtype = ("bf16", "f32")[k % 2]
+        reduction = ("mean", "sum")[(k // 2) % 2]
+        minimal = k >= n // 2
+        N = int(rng.integers(1000, 2049))
+        H = int(8 * rng.integers(16, 65))
+        # wider than one default 128 MiB panel at 1000 or more tokens (at most 65536
+        # bfloat16 or 32768 float32 entries per token)
+        V = int(rng.integers(66000, 90000)) if dtype == "bf16" else int(rng.integers(33000, 45000))
+        gl = float(np.round(rng.uniform(0.5, 2.0), 3))
+        cases.append(pytest.param(N, H, V, dtype, reduction, gl, minimal, 200 + k,
+                                  id=f"{dtype}-{reduction}-{N}x{H}x{V}-{'minws' if minimal else 'ws'}"))
+    return cases
+
+
+@pytest.mark.parametrize("N,H,V,dtype,reduction,grad_loss,minimal,seed", _random_panel_cases())
+def test_random_shapes_panels(gpu, N, H, V, dtype, reduction, grad_loss, minimal, seed):
+    """Seeded shapes large enough for several dlogit panels with the default workspace
+    (grad_x over panel pairs where all tokens form one chunk) or, with the minimum
+    workspace, many small panels and token chunks with float32 accumulators between
+    the launches; the number of dlogit launches is checked."""
+    ws = gpu.backward_min_workspace_bytes(N, H, V, torch.bfloat16 if dtype == "bf16" else torch.float32) \
+        if minimal else None
+    got = check_case(gpu, N, H, V, dtype, reduction, seed=seed, grad_loss=grad_loss, bwd_ws_bytes=ws)
+    # the plan really has several panels (and, with the minimum workspace, many)
+    x, W, t = make_inputs(N, H, V, dtype, seed=seed)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(1024)
+    w = None if ws is None else torch.empty(ws, dtype=torch.uint8, device="cuda")
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([grad_loss], device="cuda"), reduction,
+                      workspace=w, timer=bt)
+    torch.cuda.synchronize()
+    n_panels = contractions(bt).count("bwd_dlogits")
+    assert n_panels >= (4 if minimal else 2), contractions(bt)
