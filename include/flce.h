@@ -132,9 +132,11 @@ flce_status flce_forward_noalloc(const void* x, const void* W, const int64_t* ta
  * plan (at most 128 MiB, its shape chosen for these sizes), two of them when all
  * tokens form one chunk and the vocabulary takes several panels (grad_x then runs
  * once per pair), float32 accumulators where a gradient is summed over several
- * launches, and float32 partial tiles for the split tails (the tiles of a
- * launch's partial last round, cut along K and summed in a fixed order; at most
- * 256 tiles of 256 KiB).  A smaller workspace, down to
+ * launches, and float32 partial tiles: for the split tails (the tiles of a
+ * launch's partial last round, cut along K and summed in a fixed order) and, for
+ * balanced gradient launches, one partial-sum slot per workgroup plus a 4-byte
+ * flag each (the slots and flags of a shape whose launches all fill whole
+ * rounds are absent); at most 256 tiles of 256 KiB.  A smaller workspace, down to
  * flce_backward_min_workspace_bytes, makes the backward keep one panel at a time
  * or use smaller panels (more passes); a larger one changes nothing. */
 size_t flce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_dtype dt);
@@ -155,7 +157,10 @@ size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_d
  *
  * The logit tiles are recomputed from x and W; the dlogits exist only as
  * bounded panels inside `ws` (never the N x V matrix).  Deterministic: no
- * atomics, fixed accumulation order.
+ * atomic accumulation, every sum in a fixed order (of a tile whose K range two
+ * workgroups share, the one taking the head of the range starts from the
+ * other's partial sums, handed over through the workspace behind a flag), so
+ * repeated calls on one device give identical bits.
  */
 flce_status flce_backward(const void* x, const void* W, const int64_t* target,
                           const float* lse, const float* grad_loss, int64_t N, int64_t H,

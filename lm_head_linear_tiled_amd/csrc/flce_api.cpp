@@ -111,8 +111,11 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
   // dlogits, grad_W (and grad_x without K splits): full rounds of whole tiles,
   // the partial last round cut along K (kunits 256-wide units per tile) into
   // pieces, plus their float32 fixup
-  auto gw_cost = [&](int64_t tiles, int64_t kunits) {
+  auto gw_cost = [&](int64_t tiles, int64_t kunits, bool bal) {
     const int64_t g = std::min<int64_t>(tiles, cus);
+    // balanced: every workgroup the same number of slices, plus the hand-over of
+    // one partial tile per workgroup
+    if (bal && flce::balanced_launch(tiles, g)) return (double)tiles * kunits / g + kLaunch;
     const flce::TailSplit ts = flce::tail_split(tiles, g, cus);
     if (ts.kts < 2) return rounds(tiles) * kunits;
     return (double)(ts.full / g) * kunits + (double)ceil_div(kunits, ts.kts) + kLaunch +
@@ -130,8 +133,9 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
       if (cnt_v == 0) continue;
       const int64_t tm = ceil_div(Kc, kTile), tv = ceil_div(Kv, kTile);
       const int64_t ks = gx_splits_for(Nc, Vb, H);
-      const double gx = ks > 1 ? rounds(tm * th * ks) * ceil_div(tv, ks) : gw_cost(tm * th, tv);
-      double one = gw_cost(tm * tv, th) + gw_cost(tv * th, tm) + gx + 3 * kLaunch;
+      const double gx = ks > 1 ? rounds(tm * th * ks) * ceil_div(tv, ks) : gw_cost(tm * th, tv, flce::kBalance);
+      double one = gw_cost(tm * tv, th, flce::kBalanceDlogits) + gw_cost(tv * th, tm, flce::kBalance) + gx +
+                   3 * kLaunch;
       if (ks > 1) one += kLaunch + (double)(ks + 1) * Kc * H * 4 / 1e9 * kUnitsPerGB;  // partial-sum pass
       t += (double)(cnt_c * cnt_v) * one;
     }
@@ -201,22 +205,32 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   o = align_up(o + p.gxpart_bytes, 256);
   // partial tiles for the split tail of grad_W launches: the most any launch
   // shape (full or ragged chunk x full or ragged panel) needs on kPlanCUs
-  // workgroups (the launcher splits no more than this holds)
+  // workgroups (the launcher splits no more than this holds); with balanced
+  // launches, one slot per workgroup if any launch shape is balanced (the
+  // launcher balances only when its grid has no more workgroups than slots)
   p.tail_cap = 0;
+  p.slots = 0;
   const int64_t th = ceil_div(H, kTile);
-  auto need = [&](int64_t T) {
+  auto need = [&](int64_t T, bool bal) {
+    if (bal && flce::balanced_launch(T, std::min<int64_t>(T, kPlanCUs))) {
+      p.slots = kPlanCUs;
+      return;
+    }
     const flce::TailSplit ts = flce::tail_split(T, std::min<int64_t>(T, kPlanCUs), kPlanCUs);
     p.tail_cap = std::max(p.tail_cap, ts.tail * ts.kts);
   };
   for (int64_t Kv : {Vb, V - (p.n_panels - 1) * Vb}) {
-    need(ceil_div(Kv, kTile) * th);  // grad_W
-    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * ceil_div(Kv, kTile));  // dlogits
+    need(ceil_div(Kv, kTile) * th, flce::kBalance);  // grad_W
+    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc})
+      need(ceil_div(Kc, kTile) * ceil_div(Kv, kTile), flce::kBalanceDlogits);  // dlogits
   }
   if (p.gx_splits == 1)
-    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * th);  // grad_x
-  p.tail_bytes = sizeof(float) * (size_t)p.tail_cap * kTile * kTile;
+    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * th, flce::kBalance);  // grad_x
+  p.tail_bytes = sizeof(float) * (size_t)std::max(p.tail_cap, p.slots) * kTile * kTile;
   p.off_tail = o;
   o = align_up(o + p.tail_bytes, 256);
+  p.off_flags = o;
+  o = align_up(o + sizeof(int) * (size_t)p.slots, 256);
   p.total = o;
   return p;
 }
@@ -441,7 +455,8 @@ flce_status flce_backward_timed(const void* x, const void* W, const int64_t* tar
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
                                        (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
-                                       (float*)(base + p.off_tail), (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_tail), (int*)(base + p.off_flags), (hipStream_t)hip_stream,
+                                       rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -477,7 +492,8 @@ flce_status flce_backward_chunked(const void* x, const void* W, const int64_t* t
   hipError_t e = flce::launch_backward((int)dt, p, x, W, target, lse, grad_loss, red_scale, (int)N, (int)H, (int)V,
                                        grad_x, grad_W, base + p.off_panel, (float*)(base + p.off_gx),
                                        (float*)(base + p.off_gw), (float*)(base + p.off_gxpart),
-                                       (float*)(base + p.off_tail), (hipStream_t)hip_stream, rec);
+                                       (float*)(base + p.off_tail), (int*)(base + p.off_flags), (hipStream_t)hip_stream,
+                                       rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -577,7 +593,8 @@ flce_status flce_forward_backward(const void* x, const void* W, const int64_t* t
     e = flce::launch_backward((int)dt, bp, x, W, target, lse, gl,
                               reduction == FLCE_MEAN ? (float)(1.0 / (double)N) : 1.0f, (int)N, (int)H, (int)V,
                               grad_x, grad_W, base + bp.off_panel, (float*)(base + bp.off_gx),
-                              (float*)(base + bp.off_gw), (float*)(base + bp.off_gxpart), (float*)(base + bp.off_tail), s, rec);
+                              (float*)(base + bp.off_gw), (float*)(base + bp.off_gxpart), (float*)(base + bp.off_tail),
+                              (int*)(base + bp.off_flags), s, rec);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

@@ -326,6 +326,147 @@ __device__ __forceinline__ bool persistent_tile(int j, int tiles_m, int tiles_n,
   return true;
 }
 
+// Schedule of a persistent backward launch over T tiles (taken in the grouped
+// order) of KT K slices each, on the G = gridDim.x workgroups.  Unbalanced:
+// workgroup lw (XCD-grouped id) takes the whole tiles lw, lw + G, ...
+// Balanced (balanced_launch(T, G): T > G, r = T % G a nonzero multiple of
+// g = G / 8): the first R = T / G - 1 rounds go the same way, and the T' = G + r
+// tiles left form one run of T' KT slices cut evenly into G ranges of at least
+// KT slices, range p = [s0, s1) with s0 = T' KT p / G.  A tile of the run is then
+// shared by at most two ranges: the head of its K range (from k = 0) ends range
+// p, the rest of it starts range p + 1.  Range p = 8 m + x goes to workgroup m
+// of XCD x (lw = x g + m).  As T' = g D with D = 8 + r / g, range 8 m + x starts
+// at run tile D m + floor(D x / 8) and K slice (D KT x / 8) mod KT, both the
+// same for every m: the run's tile u = D m + d is taken as tile d g + m, so at
+// any time the g workgroups of an XCD work on g consecutive tiles of the grouped
+// order at the same K slice, as in a round of whole tiles, and share their
+// operand slices in the XCD's L2.  (KT D x / 8 not a whole number: ranges of one
+// XCD start up to a slice apart.)
+struct TileSched {
+  int T, KT, G, w, R;  // w: the range of a balanced run, else the XCD-grouped id
+  int D, g;            // balanced run: tiles per row, rows (= workgroups per XCD)
+  int f, k0f;          // ... this range's first run tile and its first slice
+  int e, ke;           // ... its last run tile and the end slice within it (1 .. KT)
+  __device__ __forceinline__ TileSched(int T_, int KT_, int balance) : T(T_), KT(KT_) {
+    G = (int)gridDim.x;
+    const int lw = xcd_grouped_id((int)blockIdx.x, G);
+    if (balance && balanced_launch(T, G)) {
+      R = T / G - 1;
+      g = G / 8;
+      const int Tp = T - R * G;
+      D = Tp / g;
+      w = 8 * (lw % g) + lw / g;
+      const int64_t tot = (int64_t)Tp * KT;
+      const int64_t s0 = tot * w / G, s1 = tot * (w + 1) / G;
+      f = (int)(s0 / KT);
+      k0f = (int)(s0 - (int64_t)f * KT);
+      e = (int)((s1 - 1) / KT);
+      ke = (int)(s1 - (int64_t)e * KT);
+    } else {
+      w = lw;
+      R = (T + G - 1) / G;
+      D = 1;
+      g = 1;
+      f = 0;
+      k0f = 0;
+      e = -1;
+      ke = 0;
+    }
+  }
+  // item j: tile t of the grouped order, K slices [k0, k0 + nk)
+  __device__ __forceinline__ bool item(int j, int& t, int& k0, int& nk) const {
+    if (j < R) {
+      t = w + j * G;
+      k0 = 0;
+      nk = KT;
+      return t < T;
+    }
+    const int u = f + (j - R);
+    if (u > e) return false;
+    k0 = j == R ? k0f : 0;
+    nk = (u == e ? ke : KT) - k0;
+    t = R * G + (u % D) * g + u / D;
+    return true;
+  }
+  // the head of a shared tile (finished with the partner's partial sums), and
+  // the rest of one (whose partial sums are published), from an item's K offset
+  // and slice count
+  __device__ __forceinline__ bool head(int kb, int nk) const { return kb == 0 && nk < KT; }
+  static __device__ __forceinline__ bool rest(int kb) { return kb > 0; }
+};
+
+// Float32 partial sums of a shared tile, handed from the workgroup that computes
+// the rest of its K range (publish_partial, slot and flag of its own id) to the
+// one that computes the head (take_partial, the same slot: the partner's id).  A
+// slot holds every thread's accumulators as 16-byte groups interleaved over the
+// workgroup's threads (whole 1 KiB blocks per wave and group), kTile x kTile
+// floats for 512 threads.  The slot and its flag are only written and read with
+// device-coherent accesses (written through to, and read from, the point where
+// the XCDs' caches agree), so no L2 write-back or invalidation is needed: each
+// thread waits for its slot stores to complete, the workgroup barrier orders all
+// of them before the flag store, and the reader's loads follow its flag load.
+// The head's workgroup waits for the flag before its first K slice: the rest is
+// the first item of the partner, which depends on nothing, so every wait ends
+// (the wait is also bounded: past kSpinCap polls the partial sums are taken as
+// they are).  It clears the flag again, so the flags are all 0 after each
+// launch; the launcher zeroes them once per backward.
+constexpr int kSpinCap = 1 << 20;
+constexpr int kCoherent = 16;  // buffer access cache policy: coherent across the device
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* slots, int w) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(slots + (int64_t)w * kTile * kTile), (short)0,
+                                           kTile * kTile * (int)sizeof(float), 0x00020000);
+}
+template <class G>
+__device__ __forceinline__ void publish_partial(const typename G::Acc& acc, float* __restrict__ slots,
+                                                int* __restrict__ flags, int w) {
+  static_assert(G::NT * G::FM * G::FN * G::NR <= kTile * kTile, "slot size");
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slots, w);
+  const int vo = (int)threadIdx.x * 16;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < G::NR / 4; ++g) {
+        const int q = (i * G::FN + j) * (G::NR / 4) + g;
+        const float4 v = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, vo, q * G::NT * 16, kCoherent);
+      }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
+  __syncthreads();                                   // ... and every other thread's
+  if (threadIdx.x == 0) __hip_atomic_store(flags + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class G>
+__device__ __forceinline__ void take_partial(typename G::Acc& acc, const float* __restrict__ slots,
+                                             int* __restrict__ flags, int w) {
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (__hip_atomic_load(flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && ++n < kSpinCap)
+      __builtin_amdgcn_s_sleep(2);
+    __hip_atomic_store(flags + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slots, w);
+  const int vo = (int)threadIdx.x * 16;
+  // one accumulator block (NR / 4 groups) in flight at a time
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < G::NR / 4; ++g) {
+        const int q = (i * G::FN + j) * (G::NR / 4) + g;
+        const float4 v =
+            __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, q * G::NT * 16, kCoherent));
+        acc[i][j][4 * g] += v.x;
+        acc[i][j][4 * g + 1] += v.y;
+        acc[i][j][4 * g + 2] += v.z;
+        acc[i][j][4 * g + 3] += v.w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // The dlogit kernel splits its waves into copy waves and store waves (its panel
 // stores then drain while the next tile runs).
 #ifndef FLCE_SPLIT_DLOGITS
@@ -568,7 +709,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ grad_loss, float red_scale, int N,
                                                         int H, int V, int i0, int v0, int tiles_v, int tiles_t,
-                                                        int ntiles, int Vbp, T* __restrict__ panel) {
+                                                        int ntiles, int Vbp, T* __restrict__ panel, int balance,
+                                                        float* __restrict__ slots, int* __restrict__ flags) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, K_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_DMA,
                    kSplitDlogits>
       G;
@@ -578,18 +720,34 @@ __global__ __launch_bounds__(kThreads) void bwd_dlogits(const T* __restrict__ x,
   const Operand<T> A{W, H, V, H};
   const Operand<T> B{x, H, N, H};
   const float s = grad_loss[0] * red_scale;
-  auto next = [&](int j, int& m0, int& n0) {
-    int tm, tn;
-    if (!persistent_tile<FLCE_GROUP_M_WIDE>(j, tiles_v, tiles_t, tm, tn, ntiles)) return false;
+  const TileSched sc(ntiles, (H + G::BK - 1) / G::BK, kBalanceDlogits && balance);
+  auto next = [&](int j, int& m0, int& n0, int& kb, int& nk) {
+    int t, k0, tm, tn;
+    if (!sc.item(j, t, k0, nk)) return false;
+    grouped_tile<FLCE_GROUP_M_WIDE>(t, tiles_v, tiles_t, tm, tn);
     m0 = v0 + tm * kTile;
     n0 = i0 + tn * kTile;
+    kb = k0 * G::BK;
     return true;
   };
-  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
+  // (balanced schedules only in builds with kBalanceDlogits: the hand-over
+  // pushes this kernel's registers into scratch memory)
+  auto init = [&](typename G::Acc& acc, int, int, int kb, int nk) {
+    G::zero(acc);
+    if constexpr (kBalanceDlogits)
+      if (sc.head(kb, nk)) take_partial<G>(acc, slots, flags, sc.w + 1);
+  };
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare, int kb, int) {
+    if constexpr (kBalanceDlogits)
+      if (TileSched::rest(kb)) {
+        publish_partial<G>(acc, slots, flags, sc.w);
+        return;
+      }
     dlogit_epilogue<T, G, PAIRW>(acc, m0, n0, spare, target, lse, s, N, V, i0, v0, Vbp, panel);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, H, lds, acc, next, store);
+  // items of whole slices inside H take the lean copies
+  G::run_tiles(A, B, H, lds, acc, next, store, init, true);
 }
 
 // (defined with the gradient kernels below)
@@ -754,30 +912,42 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_w(const T* __restrict__ pan
                                                        const T* __restrict__ x, int H, int V, int i0, int v0,
                                                        int Vb, int tiles_h, int tiles_v, int ntiles,
                                                        T* __restrict__ gw_out, float* __restrict__ gw_acc,
-                                                       int accumulate, int final) {
+                                                       int accumulate, int final, int balance,
+                                                       float* __restrict__ slots, int* __restrict__ flags) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, MN_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
   const int wm = G::wave_m(), wn = G::wave_n();
   const Operand<T> A{x + (int64_t)i0 * H, H, H, Kc};
   const Operand<T> B{panel, Vbp, Vbp, Kc};
-  auto next = [&](int j, int& m0, int& n0) {
-    int tm, tn;
-    if (!persistent_tile(j, tiles_h, tiles_v, tm, tn, ntiles)) return false;
+  const TileSched sc(ntiles, (Kc + G::BK - 1) / G::BK, balance);
+  auto next = [&](int j, int& m0, int& n0, int& kb, int& nk) {
+    int t, k0, tm, tn;
+    if (!sc.item(j, t, k0, nk)) return false;
+    grouped_tile(t, tiles_h, tiles_v, tm, tn);
     m0 = tm * kTile;
     n0 = tn * kTile;
+    kb = k0 * G::BK;
     return true;
   };
   auto row_ok = [&](int v) { return v < Vb && v0 + v < V; };
   auto row_off = [&](int v) { return (int64_t)v * H; };
-  auto init = [&](typename G::Acc& acc, int m0, int n0) {
-    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate, gw_acc, row_ok, row_off);
+  auto init = [&](typename G::Acc& acc, int m0, int n0, int kb, int nk) {
+    // the rest of a shared tile starts from zero; the head from the earlier
+    // launches' sums plus the rest's partial sums
+    grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate && !TileSched::rest(kb), gw_acc, row_ok,
+                 row_off);
+    if (sc.head(kb, nk)) take_partial<G>(acc, slots, flags, sc.w + 1);
   };
-  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare) {
-    grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gw_out, gw_acc, row_ok, row_off);
+  auto store = [&](typename G::Acc& acc, int m0, int n0, char* spare, int kb, int) {
+    if (TileSched::rest(kb))
+      publish_partial<G>(acc, slots, flags, sc.w);
+    else
+      grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gw_out, gw_acc, row_ok, row_off);
   };
   typename G::Acc acc;
-  G::run_tiles(A, B, Kc, lds, acc, next, store, init);
+  // items of whole slices inside the chunk take the lean copies
+  G::run_tiles(A, B, Kc, lds, acc, next, store, init, true);
 }
 
 // The split tail of a gradient launch (the tiles full .. of its grouped order
@@ -886,7 +1056,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
                                                        int tiles_h, int tiles_t, int ks, int Ks, int Ncp,
                                                        T* __restrict__ gx_out, float* __restrict__ gx_acc,
                                                        float* __restrict__ part, int accumulate, int final,
-                                                       int nitems) {
+                                                       int nitems, int balance, float* __restrict__ slots,
+                                                       int* __restrict__ flags) {
   typedef TileGemm<T, kTile, kTile, Cfg<T>::BK, MN_MAJOR, K_MAJOR, Cfg<T>::NS, FLCE_WAVES_M, FLCE_WAVES_N, STAGE_REG>
       G;
   __shared__ __attribute__((aligned(16))) T lds[G::LDS_ELEMS];
@@ -934,13 +1105,30 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_x(const T* __restrict__ pan
   };
   typename G::Acc acc;
   if (ks == 1) {
-    // one split: tiles start at K offset 0, which lets whole-slice copies take
-    // the lean form
-    auto next1 = [&](int j, int& m0, int& n0) {
-      int s;
-      return item(j, s, m0, n0);
+    // one split: the schedule of bwd_grad_w over the launch's tiles
+    const TileSched sc(nitems, (Ks + G::BK - 1) / G::BK, balance);
+    auto next1 = [&](int j, int& m0, int& n0, int& kb, int& nk) {
+      int t, k0, tm, tn;
+      if (!sc.item(j, t, k0, nk)) return false;
+      grouped_tile<FLCE_GROUP_M_WIDE>(t, tiles_h, tiles_t, tm, tn);
+      m0 = tm * kTile;
+      n0 = tn * kTile;
+      kb = k0 * G::BK;
+      return true;
     };
-    G::run_tiles(A, B, Ks, lds, acc, next1, store, init);
+    auto init1 = [&](typename G::Acc& acc, int m0, int n0, int kb, int nk) {
+      grad_init<G>(acc, m0 + wm * G::WM, n0 + wn * G::WN, H, accumulate && !TileSched::rest(kb), gx_acc, row_ok,
+                   row_off);
+      if (sc.head(kb, nk)) take_partial<G>(acc, slots, flags, sc.w + 1);
+    };
+    auto store1 = [&](typename G::Acc& acc, int m0, int n0, char* spare, int kb, int) {
+      if (TileSched::rest(kb))
+        publish_partial<G>(acc, slots, flags, sc.w);
+      else
+        grad_epilogue<T, G>(acc, spare, m0 + wm * G::WM, n0 + wn * G::WN, H, final, gx_out, gx_acc, row_ok, row_off);
+    };
+    // items of whole slices inside the group's entries take the lean copies
+    G::run_tiles(A, B, Ks, lds, acc, next1, store1, init1, true);
   } else {
     // splits of whole slices that end at the group's last entry exactly take
     // the lean copies too
@@ -1214,7 +1402,7 @@ template <typename T>
 static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv, const int64_t* target,
                                const float* lse, const float* grad_loss, float red_scale, int N, int H, int V,
                                void* gxv, void* gwv, void* panelv, float* gx_acc, float* gw_acc, float* gx_part,
-                               float* tail_buf, hipStream_t st, Recorder& rec) {
+                               float* tail_buf, int* flags, hipStream_t st, Recorder& rec) {
   const T* x = (const T*)xv;
   const T* W = (const T*)Wv;
   T* gx = (T*)gxv;
@@ -1226,6 +1414,11 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
   float* gwa0 = f32 ? (float*)gwv : gw_acc;  // [V, H] in place, or one panel [Vb, H]
   const int tiles_h = (H + kTile - 1) / kTile;
   rec.start();
+  // balanced launches need a partial-sum slot per workgroup; their flags start
+  // at 0 (each launch leaves them so)
+  const bool can_balance = p.slots > 0 && p.max_workgroups <= p.slots;
+  if (can_balance) hipLaunchKernelGGL(zero_f32, dim3(1), dim3(256), 0, st, (float*)flags, (int64_t)p.slots);
+  auto balance = [&](bool on, int T_, int G_) { return on && can_balance && balanced_launch(T_, G_) ? 1 : 0; };
   for (int pv = 0; pv < p.n_panels; ++pv) {
     const int v0 = pv * p.Vb;
     const int Kv = min(p.Vb, V - v0);
@@ -1249,9 +1442,10 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
         constexpr int BK = Cfg<T>::BK;
         const int T_ = tiles_m * tiles_n;
         const dim3 g = grid(T_);
-        const Tail tl = plan_tail(T_, g.x, p.tail_cap, (H + BK - 1) / BK, BK);
+        const int bal = balance(kBalanceDlogits, T_, (int)g.x);
+        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, g.x, p.tail_cap, (H + BK - 1) / BK, BK);
         hipLaunchKernelGGL(bwd_dlogits<T>, g, dim3(kThreads), 0, st, x, W, target, lse, grad_loss, red_scale, N, H,
-                           V, i0, v0, tiles_n, tiles_m, T_ - tl.tail, Vbp, sub);
+                           V, i0, v0, tiles_n, tiles_m, T_ - tl.tail, Vbp, sub, bal, tail_buf, flags);
         rec.after(FLCE_K_BWD_DLOGITS);
         if (tl.tail) {
           hipLaunchKernelGGL(bwd_dlogit_pieces<T>, dim3(tl.tail * tl.kts), dim3(kThreads), 0, st, x, W, N, H, V, i0,
@@ -1270,10 +1464,12 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
         constexpr int BK = Cfg<T>::BK;
         const int T_ = tiles_n * tiles_h;
         const dim3 g = grid(T_);
-        const Tail tl = plan_tail(T_, g.x, p.tail_cap, (Kc + BK - 1) / BK, BK);
+        const int bal = balance(kBalance, T_, (int)g.x);
+        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, g.x, p.tail_cap, (Kc + BK - 1) / BK, BK);
         const int acc_w = c > 0 ? 1 : 0, fin_w = c == p.n_chunks - 1 ? 1 : 0;
         hipLaunchKernelGGL(bwd_grad_w<T>, g, dim3(kThreads), 0, st, (const T*)sub, Vbp, Kc, x, H, V, i0, v0, Kv,
-                           tiles_h, tiles_n, T_ - tl.tail, gw + (int64_t)v0 * H, gwa, acc_w, fin_w);
+                           tiles_h, tiles_n, T_ - tl.tail, gw + (int64_t)v0 * H, gwa, acc_w, fin_w, bal, tail_buf,
+                           flags);
         rec.after(FLCE_K_BWD_GRAD_W);
         if (tl.tail) {
           hipLaunchKernelGGL((bwd_grad_pieces<T, true, FLCE_GROUP_M>), dim3(tl.tail * tl.kts), dim3(kThreads), 0, st,
@@ -1296,9 +1492,11 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       // without K splits, the partial last round of tiles is cut along K instead
       const int Tx = tiles_m * tiles_h;
       const dim3 gxg = grid(Tx * ks);
-      const Tail tl = ks == 1 ? plan_tail(Tx, gxg.x, p.tail_cap, Ks / BK, BK) : Tail{0, 0, 0};
+      const int balx = ks == 1 ? balance(kBalance, Tx, (int)gxg.x) : 0;
+      const Tail tl = ks == 1 && !balx ? plan_tail(Tx, gxg.x, p.tail_cap, Ks / BK, BK) : Tail{0, 0, 0};
       hipLaunchKernelGGL(bwd_grad_x<T>, gxg, dim3(kThreads), 0, st, (const T*)panel, Vbp, Kgp, Kc, Kg, W, H, N, i0,
-                         gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x, Tx * ks - tl.tail);
+                         gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x, Tx * ks - tl.tail,
+                         balx, tail_buf, flags);
       rec.after(FLCE_K_BWD_GRAD_X);
       if (tl.tail) {
         hipLaunchKernelGGL((bwd_grad_pieces<T, false, FLCE_GROUP_M_WIDE>), dim3(tl.tail * tl.kts), dim3(kThreads), 0,
@@ -1371,11 +1569,11 @@ hipError_t launch_backward_atomic(int dt, const void* x, const void* W, const in
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
                            void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, float* tail,
-                           hipStream_t st, Recorder& rec) {
+                           int* flags, hipStream_t st, Recorder& rec) {
   return dt == 1 ? launch_bwd_t<bf16_t>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                        gw_acc, gx_part, tail, st, rec)
+                                        gw_acc, gx_part, tail, flags, st, rec)
                  : launch_bwd_t<float>(p, x, W, target, lse, grad_loss, red_scale, N, H, V, gx, gw, panel, gx_acc,
-                                       gw_acc, gx_part, tail, st, rec);
+                                       gw_acc, gx_part, tail, flags, st, rec);
 }
 
 }  // namespace flce

@@ -30,7 +30,8 @@ struct BwdPlan {
   int Ncp;                  // Nc padded to kTile
   int gx_splits;            // grad_x K splits per launch (1: none), partial sums in gxpart
   int tail_cap;             // float32 256 x 256 partial tiles for split tail tiles of grad_W launches
-  size_t off_panel, off_gx, off_gw, off_gxpart, off_tail, total;  // workspace carving (bytes); 0-sized parts unused
+  int slots;                // balanced launches: float32 256 x 256 partial-sum slots (one per workgroup) and flags
+  size_t off_panel, off_gx, off_gw, off_gxpart, off_tail, off_flags, total;  // workspace carving (bytes); 0-sized parts unused
   size_t gx_bytes, gw_bytes, gxpart_bytes, tail_bytes;
   int max_workgroups;                       // persistent grid size: one workgroup per CU
 };
@@ -88,7 +89,25 @@ hipError_t static_scratch(void** out);
 hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* W, const int64_t* target,
                            const float* lse, const float* grad_loss, float red_scale, int N, int H, int V, void* gx,
                            void* gw, void* panel, float* gx_acc, float* gw_acc, float* gx_part, float* tail,
-                           hipStream_t st, Recorder& rec);
+                           int* flags, hipStream_t st, Recorder& rec);
+
+// Balanced schedules of the gradient launches (a launch of T > G tiles on G
+// workgroups, T % G a nonzero multiple of G / 8, cuts its last T - (T / G - 1) G
+// tiles evenly along K over all workgroups, keeping each XCD's workgroups at
+// one K offset; the partial sums of a tile shared by two workgroups pass
+// through one slot per workgroup); the dlogit launches only in builds with
+// FLCE_BALANCE_DLOGITS.  Otherwise the partial last round is split into K pieces.
+#ifndef FLCE_BALANCE
+#define FLCE_BALANCE 1
+#endif
+#ifndef FLCE_BALANCE_DLOGITS
+#define FLCE_BALANCE_DLOGITS 0
+#endif
+constexpr bool kBalance = FLCE_BALANCE != 0;
+constexpr bool kBalanceDlogits = kBalance && FLCE_BALANCE_DLOGITS != 0;
+__host__ __device__ inline bool balanced_launch(int64_t T, int64_t G) {
+  return G > 0 && G % 8 == 0 && T > G && T % G != 0 && (T % G) % (G / 8) == 0;
+}
 
 // Split of the last, partial round of a persistent launch of T tiles on G
 // workgroups: the T - T % G tiles of the full rounds are done whole; the tail

@@ -593,11 +593,17 @@ struct TileGemm {
   // it returns (the next slice's copies into it start after the barrier that
   // opens that slice).  Every wave of the workgroup calls epi for the same tiles.
   // Ends with a barrier: the caller may reuse the LDS afterwards.
-  // next(j, m0, n0) or next(j, m0, n0, kb): the second form also gives the K
-  // offset at which the tile's K range of length K starts (split-K tiles).
+  // next(j, m0, n0), next(j, m0, n0, kb) or next(j, m0, n0, kb, nk): the second
+  // form also gives the K offset at which the tile's K range of length K starts
+  // (split-K tiles), the third the K offset and the number of K slices of the
+  // item (at least one; segments of a tile's K range, kb + nk BK <= the K
+  // given to run_tiles rounded up to BK).
+  // (nk is written by the third form only)
   template <class Next>
-  static __device__ __forceinline__ bool next_tile(Next& next, int j, int& m0, int& n0, int& kb) {
-    if constexpr (std::is_invocable_v<Next&, int, int&, int&, int&>) {
+  static __device__ __forceinline__ bool next_tile(Next& next, int j, int& m0, int& n0, int& kb, int& nk) {
+    if constexpr (std::is_invocable_v<Next&, int, int&, int&, int&, int&>) {
+      return next(j, m0, n0, kb, nk);
+    } else if constexpr (std::is_invocable_v<Next&, int, int&, int&, int&>) {
       return next(j, m0, n0, kb);
     } else {
       kb = 0;
@@ -605,10 +611,28 @@ struct TileGemm {
     }
   }
 
-  // k_whole (split-K sequences, next(j, m0, n0, kb) only): the caller guarantees
-  // that every tile's K range [kb, kb + K) lies inside both operands' K extents
-  // with kb a multiple of BK (so no slice straddles an operand's block split,
-  // itself a multiple of BK), which lets those sequences take the lean copies too.
+  // init(acc, m0, n0) and epi(acc, m0, n0, spare) may also take the item's K
+  // offset and number of K slices as two more arguments.
+  template <class Init>
+  static __device__ __forceinline__ void call_init(Init& init, Acc& acc, int m0, int n0, int kb, int nk) {
+    if constexpr (std::is_invocable_v<Init&, Acc&, int, int, int, int>)
+      init(acc, m0, n0, kb, nk);
+    else
+      init(acc, m0, n0);
+  }
+  template <class Epi>
+  static __device__ __forceinline__ void call_epi(Epi& epi, Acc& acc, int m0, int n0, char* spare, int kb, int nk) {
+    if constexpr (std::is_invocable_v<Epi&, Acc&, int, int, char*, int, int>)
+      epi(acc, m0, n0, spare, kb, nk);
+    else
+      epi(acc, m0, n0, spare);
+  }
+
+  // k_whole (split-K sequences, next with a K offset only): the caller guarantees
+  // that every item's K range ([kb, kb + K), or [kb, kb + nk BK)) lies inside
+  // both operands' K extents with kb a multiple of BK (so no slice straddles an
+  // operand's block split, itself a multiple of BK), which lets those sequences
+  // take the lean copies too.
   template <class Next, class Epi, class Init>
   static __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int K, T* lds, Acc& acc,
                                                    Next&& next, Epi&& epi, Init&& init, bool k_whole = false) {
@@ -617,7 +641,8 @@ struct TileGemm {
     // ranges -- and each operand is either K-major with its K range inside its
     // rows, or (register staging only) MN-major with every tile inside its mn range.
     constexpr bool LEAN_OK = STAGING == STAGE_REG || (AMAJ == K_MAJOR && BMAJ == K_MAJOR);
-    constexpr bool SPLIT_K = std::is_invocable_v<Next&, int, int&, int&, int&>;
+    constexpr bool SPLIT_K = std::is_invocable_v<Next&, int, int&, int&, int&> ||
+                             std::is_invocable_v<Next&, int, int&, int&, int&, int&>;
     auto fits = [&](const Operand<T>& op, bool kmajor, int MNT) {
       if (op.k_ext < K) return false;
       const int k1 = op.k_ext < op.ksplit ? op.k_ext : op.ksplit;  // K extent of the widest block
@@ -637,13 +662,16 @@ struct TileGemm {
                                                         Acc& acc, Next&& next, Epi&& epi, Init&& init) {
     static_assert(NSTAGE == 2, "the persistent loop double-buffers K slices");
     constexpr int AOFF = A_BYTES / ES;
+    // items with their own slice counts (next with five arguments); otherwise
+    // every item has KT slices
+    constexpr bool SEG = std::is_invocable_v<Next&, int, int&, int&, int&, int&>;
     const int KT = (K + BK - 1) / BK;
-    int tm0, tn0, tkb;
-    if (!next_tile(next, 0, tm0, tn0, tkb)) return;
-    // copy cursor: slice pk of tile pj, origin (pm0, pn0), K offset pkb; past the
-    // last tile it points at K offset KT * BK, and its copies (into a stage no
-    // slice reads) stay inside the operands or read zeros
-    int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0, pkb = tkb;
+    int tm0, tn0, tkb, tkt = KT;
+    if (!next_tile(next, 0, tm0, tn0, tkb, tkt)) return;
+    // copy cursor: slice pk of tile pj (pkt slices), origin (pm0, pn0), K offset
+    // pkb; past the last tile it points at K offset KT * BK, and its copies (into
+    // a stage no slice reads) stay inside the operands or read zeros
+    int pj = 0, pk = 0, pm0 = tm0, pn0 = tn0, pkb = tkb, pkt = tkt;
     bool pvalid = true;
     const bool cw = copy_wave();
     if (cw) {
@@ -651,17 +679,21 @@ struct TileGemm {
       load_tile<BMAJ, BN>(B, pn0, pkb, lds + AOFF);
     }
     auto advance = [&]() {
-      if (++pk == KT) {
+      if (++pk == (SEG ? pkt : KT)) {
         pk = 0;
         ++pj;
-        pvalid = pvalid && next_tile(next, pj, pm0, pn0, pkb);
+        pvalid = pvalid && next_tile(next, pj, pm0, pn0, pkb, pkt);
       }
     };
     advance();
-    init(acc, tm0, tn0);
+    if constexpr (SEG)
+      call_init(init, acc, tm0, tn0, tkb, tkt);
+    else
+      init(acc, tm0, tn0);
     int q = 0;
     for (int j = 0;;) {
-      for (int kt = 0; kt < KT; ++kt, ++q) {
+      const int nkt = SEG ? tkt : KT;
+      for (int kt = 0; kt < nkt; ++kt, ++q) {
         // After an epilogue only LDS work is drained: every wave waited for its
         // copies of this slice before the epilogue, so the global stores the
         // epilogue issued stay in flight.
@@ -682,9 +714,15 @@ struct TileGemm {
       // this wave's copies of the next tile's first slice have landed (a wave
       // without copies leaves its stores in flight)
       if (cw) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
-      if (!next_tile(next, ++j, tm0, tn0, tkb)) break;
-      init(acc, tm0, tn0);
+      if constexpr (SEG)
+        call_epi(epi, acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES, tkb, tkt);
+      else
+        epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
+      if (!next_tile(next, ++j, tm0, tn0, tkb, tkt)) break;
+      if constexpr (SEG)
+        call_init(init, acc, tm0, tn0, tkb, tkt);
+      else
+        init(acc, tm0, tn0);
     }
     wait_and_barrier<0>();
   }

@@ -337,19 +337,31 @@ def test_out_of_range_targets(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_grad_w_tail_split(gpu, dtype):
-    """A grad_W launch of 157 vocabulary x 2 hidden tiles = 314 tiles on 256
-    workgroups: 256 whole tiles, and the 58 tiles of the partial last round cut
-    along K (600 tokens) into pieces (their own launch), summed by the tail fixup."""
-    N, H, V = 600, 512, 40000
+@pytest.mark.parametrize("V", [8000, 16300])
+def test_grad_w_balanced(gpu, dtype, V):
+    """A grad_W launch of 9 hidden x 32 (V 8000) or 64 (V 16300) vocabulary tiles =
+    288 or 576 tiles on 256 workgroups, K = 600 tokens (a ragged last slice): 288
+    % 256 = 576 % 256 - 32 = 32 is a multiple of 256 / 8, so the launch is
+    balanced -- no round of whole tiles (288) or one (576), then the remaining 288
+    or 320 tiles cut evenly along K over the 256 workgroups, each XCD's
+    workgroups at one K offset, tiles shared by two workgroups summed through a
+    partial-sum slot -- and needs no split-tail launches after it."""
+    N, H = 600, 2304
     got = check_case(gpu, N, H, V, dtype, "sum", seed=71, grad_loss=0.8)
     x, W, t = make_inputs(N, H, V, dtype, seed=71)
     xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
     bt = gpu.KernelTimer(32)
-    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.8], device="cuda"), "sum", timer=bt)
+    gx, gW = gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.8], device="cuda"), "sum", timer=bt)
     torch.cuda.synchronize()
     seq = contractions(bt)
-    assert seq[:4] == ["bwd_dlogits", "bwd_grad_w", "tail_pieces", "tail_fixup"], seq
+    assert seq[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"], seq
+    # the same bits again (the shared tiles' sums do not depend on timing)
+    gx2, gW2 = gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.8], device="cuda"), "sum")
+    torch.cuda.synchronize()
+    assert torch.equal(gW.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       gW2.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(gx.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       gx2.view(torch.int16 if dtype == "bf16" else torch.int32))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -358,8 +370,9 @@ def test_whole_slice_splits(gpu, dtype):
     (these take the lean copies): one 36864-entry panel of 144 vocabulary tiles,
     512 hidden; the dlogit launch's 4 x 144 (bf16: 1024 tokens) or 2 x 144 (fp32:
     512 tokens) logit tiles leave 64 / 32 tail tiles cut along H into 4 / 8
-    pieces, grad_W's 288 tiles leave 32 cut along the tokens into 8 pieces, and
-    grad_x (8 or 4 output tiles) is split 4 ways over the vocabulary."""
+    pieces, grad_W's 288 tiles are balanced (cut evenly along the tokens over the
+    256 workgroups), and grad_x (8 or 4 output tiles) is split 4 ways over the
+    vocabulary."""
     N, H, V = (1024 if dtype == "bf16" else 512), 512, 36864
     got = check_case(gpu, N, H, V, dtype, "mean", seed=74, grad_loss=1.1)
     x, W, t = make_inputs(N, H, V, dtype, seed=74)
@@ -368,36 +381,34 @@ def test_whole_slice_splits(gpu, dtype):
     gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.1], device="cuda"), "mean", timer=bt)
     torch.cuda.synchronize()
     seq = contractions(bt)
-    assert seq == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "tail_pieces", "tail_fixup",
-                   "bwd_grad_x", "bwd_gx_reduce"], seq
+    assert seq == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "bwd_grad_x", "bwd_gx_reduce"], seq
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("panels", [1, 3])
-def test_grad_x_tail_split(gpu, dtype, panels):
-    """A grad_x launch of 16 token x 17 hidden tiles = 272 tiles on 256
-    workgroups (no K split of all tiles): the 16 tiles of the partial last round
-    are cut along K (vocabulary) into pieces.  With three vocabulary panels (V =
-    20000 fp32 / 40000 bf16: 8192 / 16384 entries per 128 MiB panel of 4096
-    tokens) grad_x runs once per pair of panels: the second launch's pieces are
-    added to the first's float32 sums and written in the output type."""
-    N, H = 4000, 4352
+def test_grad_x_balanced(gpu, dtype, panels):
+    """A grad_x launch of 16 token x 18 hidden tiles = 288 tiles on 256
+    workgroups (no K split of all tiles) is balanced: its tiles cut evenly along K
+    (vocabulary) over the workgroups, 32 of them shared by two.  With three
+    vocabulary panels (V = 20000 fp32 / 40000 bf16: 8192 / 16384 entries per 128
+    MiB panel of 4096 tokens) grad_x runs once per pair of panels: the second
+    launch's shared tiles start from the first's float32 sums and are written in
+    the output type; the full panels' grad_W launches (18 x 32 or 18 x 64 tiles)
+    are balanced after three or one rounds of whole tiles."""
+    N, H = 4000, 4608
     V = 3000 if panels == 1 else (20000 if dtype == "f32" else 40000)
-    ws = None
-    got = check_case(gpu, N, H, V, dtype, "mean", seed=72, grad_loss=1.3, bwd_ws_bytes=ws)
+    got = check_case(gpu, N, H, V, dtype, "mean", seed=72, grad_loss=1.3)
     x, W, t = make_inputs(N, H, V, dtype, seed=72)
     xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
     bt = gpu.KernelTimer(256)
-    w = None if ws is None else torch.empty(ws, dtype=torch.uint8, device="cuda")
-    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.3], device="cuda"), "mean", workspace=w,
-                      timer=bt)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.3], device="cuda"), "mean", timer=bt)
     torch.cuda.synchronize()
     seq = contractions(bt)
-    fixups_after_gx = sum(1 for a, b, c in zip(seq, seq[1:], seq[2:])
-                          if (a, b, c) == ("bwd_grad_x", "tail_pieces", "tail_fixup"))
-    assert fixups_after_gx >= 1, seq
+    assert seq.count("bwd_grad_x") == (1 if panels == 1 else 2), seq
+    assert "bwd_gx_reduce" not in seq, seq
+    assert all(b != "tail_pieces" for a, b in zip(seq, seq[1:]) if a == "bwd_grad_x"), seq
     if panels > 1:
-        assert seq.count("bwd_grad_x") >= 2, seq
+        assert seq[:2] == ["bwd_dlogits", "bwd_grad_w"] and seq[2] != "tail_pieces", seq
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
