@@ -116,7 +116,7 @@ double backward_cost(int64_t N, int64_t H, int64_t V, int64_t Nc, int64_t Vb, in
     // balanced: every workgroup the same number of slices, plus the hand-over of
     // one partial tile per workgroup
     if (bal && flce::balanced_launch(tiles, g)) return (double)tiles * kunits / g + kLaunch;
-    const flce::TailSplit ts = flce::tail_split(tiles, g, cus);
+    const flce::TailSplit ts = flce::tail_split(tiles, cus, cus, kunits * kTile);
     if (ts.kts < 2) return rounds(tiles) * kunits;
     return (double)(ts.full / g) * kunits + (double)ceil_div(kunits, ts.kts) + kLaunch +
            (double)ts.tail * (ts.kts + 2) * kTile * kTile * 4 / 1e9 * kUnitsPerGB;
@@ -211,21 +211,27 @@ BwdPlan plan_backward_shape(int64_t N, int64_t H, int64_t V, flce_dtype dt, int6
   p.tail_cap = 0;
   p.slots = 0;
   const int64_t th = ceil_div(H, kTile);
-  auto need = [&](int64_t T, bool bal) {
+  auto need = [&](int64_t T, int64_t K, bool bal) {
     if (bal && flce::balanced_launch(T, std::min<int64_t>(T, kPlanCUs))) {
       p.slots = kPlanCUs;
       return;
     }
-    const flce::TailSplit ts = flce::tail_split(T, std::min<int64_t>(T, kPlanCUs), kPlanCUs);
+    const flce::TailSplit ts = flce::tail_split(T, kPlanCUs, kPlanCUs, K);
     p.tail_cap = std::max(p.tail_cap, ts.tail * ts.kts);
   };
-  for (int64_t Kv : {Vb, V - (p.n_panels - 1) * Vb}) {
-    need(ceil_div(Kv, kTile) * th, flce::kBalance);  // grad_W
-    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc})
-      need(ceil_div(Kc, kTile) * ceil_div(Kv, kTile), flce::kBalanceDlogits);  // dlogits
+  const int64_t Kv_last = V - (p.n_panels - 1) * Vb, Kc_last = N - (p.n_chunks - 1) * Nc;
+  for (int64_t Kv : {Vb, Kv_last})
+    for (int64_t Kc : {Nc, Kc_last}) {
+      need(ceil_div(Kv, kTile) * th, Kc, flce::kBalance);                                  // grad_W
+      need(ceil_div(Kc, kTile) * ceil_div(Kv, kTile), H, flce::kBalanceDlogits);           // dlogits
+    }
+  if (p.gx_splits == 1) {
+    // grad_x K: a whole group of panels, or the last group (it holds the last panel)
+    const int64_t Kg_last = V - (int64_t)((p.n_panels - 1) / p.gx_group) * p.gx_group * Vb;
+    for (int64_t Kc : {Nc, Kc_last})
+      for (int64_t Kg : {std::min<int64_t>((int64_t)p.gx_group * Vb, V), Kg_last})
+        need(ceil_div(Kc, kTile) * th, Kg, flce::kBalance);
   }
-  if (p.gx_splits == 1)
-    for (int64_t Kc : {Nc, N - (p.n_chunks - 1) * Nc}) need(ceil_div(Kc, kTile) * th, flce::kBalance);  // grad_x
   p.tail_bytes = sizeof(float) * (size_t)std::max(p.tail_cap, p.slots) * kTile * kTile;
   p.off_tail = o;
   o = align_up(o + p.tail_bytes, 256);

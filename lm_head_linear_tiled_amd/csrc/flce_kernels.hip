@@ -1383,14 +1383,15 @@ hipError_t launch_forward(int dt, const FwdPlan& p, const void* x, const void* W
                                        rec);
 }
 
-// The tail split of one gradient launch (T tiles on G workgroups, KT K slices of
-// BK per tile): tail tiles, pieces per tail tile, K extent per piece (a whole
-// number of slices); tail = 0: no split.
+// The tail split of one backward launch (T tiles on `cus` workgroups, KT K slices
+// of BK per tile): tail tiles, pieces per tail tile, K extent per piece (a whole
+// number of slices); tail = 0: no split.  With tail = T (a launch of few tiles)
+// the main launch has no tiles and runs as a single idle workgroup.
 struct Tail {
   int tail, kts, Kp;
 };
-static Tail plan_tail(int T, int G, int cap, int KT, int BK) {
-  const TailSplit ts = tail_split(T, G, cap);
+static Tail plan_tail(int T, int cus, int cap, int KT, int BK) {
+  const TailSplit ts = tail_split(T, cus, cap, (int64_t)KT * BK);
   if (ts.kts < 2) return Tail{0, 0, 0};
   const int per = (KT + ts.kts - 1) / ts.kts;  // K slices per piece
   const int kts = (KT + per - 1) / per;
@@ -1441,9 +1442,9 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
         // the partial last round of logit tiles is cut along K (hidden) into pieces
         constexpr int BK = Cfg<T>::BK;
         const int T_ = tiles_m * tiles_n;
-        const dim3 g = grid(T_);
-        const int bal = balance(kBalanceDlogits, T_, (int)g.x);
-        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, g.x, p.tail_cap, (H + BK - 1) / BK, BK);
+        const int bal = balance(kBalanceDlogits, T_, (int)grid(T_).x);
+        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, p.max_workgroups, p.tail_cap, (H + BK - 1) / BK, BK);
+        const dim3 g = grid(tl.tail < T_ ? T_ : 1);
         hipLaunchKernelGGL(bwd_dlogits<T>, g, dim3(kThreads), 0, st, x, W, target, lse, grad_loss, red_scale, N, H,
                            V, i0, v0, tiles_n, tiles_m, T_ - tl.tail, Vbp, sub, bal, tail_buf, flags);
         rec.after(FLCE_K_BWD_DLOGITS);
@@ -1463,9 +1464,9 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
         // the partial last round of tiles is cut along K (tokens) into pieces
         constexpr int BK = Cfg<T>::BK;
         const int T_ = tiles_n * tiles_h;
-        const dim3 g = grid(T_);
-        const int bal = balance(kBalance, T_, (int)g.x);
-        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, g.x, p.tail_cap, (Kc + BK - 1) / BK, BK);
+        const int bal = balance(kBalance, T_, (int)grid(T_).x);
+        const Tail tl = bal ? Tail{0, 0, 0} : plan_tail(T_, p.max_workgroups, p.tail_cap, (Kc + BK - 1) / BK, BK);
+        const dim3 g = grid(tl.tail < T_ ? T_ : 1);
         const int acc_w = c > 0 ? 1 : 0, fin_w = c == p.n_chunks - 1 ? 1 : 0;
         hipLaunchKernelGGL(bwd_grad_w<T>, g, dim3(kThreads), 0, st, (const T*)sub, Vbp, Kc, x, H, V, i0, v0, Kv,
                            tiles_h, tiles_n, T_ - tl.tail, gw + (int64_t)v0 * H, gwa, acc_w, fin_w, bal, tail_buf,
@@ -1491,9 +1492,9 @@ static hipError_t launch_bwd_t(const BwdPlan& p, const void* xv, const void* Wv,
       const int acc_x = gv0 > 0 ? 1 : 0, fin_x = pv == p.n_panels - 1 ? 1 : 0;
       // without K splits, the partial last round of tiles is cut along K instead
       const int Tx = tiles_m * tiles_h;
-      const dim3 gxg = grid(Tx * ks);
-      const int balx = ks == 1 ? balance(kBalance, Tx, (int)gxg.x) : 0;
-      const Tail tl = ks == 1 && !balx ? plan_tail(Tx, gxg.x, p.tail_cap, Ks / BK, BK) : Tail{0, 0, 0};
+      const int balx = ks == 1 ? balance(kBalance, Tx, (int)grid(Tx).x) : 0;
+      const Tail tl = ks == 1 && !balx ? plan_tail(Tx, p.max_workgroups, p.tail_cap, Ks / BK, BK) : Tail{0, 0, 0};
+      const dim3 gxg = grid(tl.tail < Tx * ks ? Tx * ks : 1);
       hipLaunchKernelGGL(bwd_grad_x<T>, gxg, dim3(kThreads), 0, st, (const T*)panel, Vbp, Kgp, Kc, Kg, W, H, N, i0,
                          gv0, tiles_h, tiles_m, ks, Ks, p.Ncp, gx, gxa, gx_part, acc_x, fin_x, Tx * ks - tl.tail,
                          balx, tail_buf, flags);

@@ -109,17 +109,27 @@ __host__ __device__ inline bool balanced_launch(int64_t T, int64_t G) {
   return G > 0 && G % 8 == 0 && T > G && T % G != 0 && (T % G) % (G / 8) == 0;
 }
 
-// Split of the last, partial round of a persistent launch of T tiles on G
-// workgroups: the T - T % G tiles of the full rounds are done whole; the tail
-// (T % G tiles) is cut along K into kts pieces each when at least two pieces per
-// tail tile fit in the G workgroups and in `cap` partial-tile buffers (kts = 0:
-// no split).  Shared by the planner (workspace size) and the launcher.
+// Split of the last, partial round of a persistent launch of T tiles of K
+// entries along K on `cus` workgroups: the T - T % cus tiles of the full rounds
+// are done whole; the tail (T % cus tiles) is cut along K into kts pieces each
+// when at least two pieces per tail tile fit in the workgroups and in `cap`
+// partial-tile buffers (kts = 0: no split).  A launch of few tiles (T <= cus / 2,
+// at least 1024 entries of K) is all tail: each tile cut into kts >= 2 pieces,
+// so that the idle CUs share its work.  Shared by the planner (workspace size)
+// and the launcher.
 struct TailSplit {
   int full, tail, kts;
 };
-inline TailSplit tail_split(int64_t T, int64_t G, int cap) {
+inline TailSplit tail_split(int64_t T, int64_t cus, int cap, int64_t K) {
   TailSplit s{(int)T, 0, 0};
-  if (G <= 0 || T <= 0) return s;
+  if (cus <= 0 || T <= 0) return s;
+  const int64_t room = std::min<int64_t>(cus, cap);
+  if (2 * T <= cus && K >= 1024) {
+    const int64_t kts = room / T;
+    if (kts >= 2) s = TailSplit{0, (int)T, (int)kts};
+    return s;
+  }
+  const int64_t G = std::min<int64_t>(T, cus);
   const int64_t tail = T % G;
   if (tail == 0) return s;
   const int64_t kts = std::min<int64_t>(G, cap) / tail;

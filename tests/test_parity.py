@@ -294,7 +294,9 @@ def test_timed_variants_record_every_kernel(gpu):
     fk = [k for k, _ in ft.durations()]
     assert fk == ["fwd_partial", "fwd_combine"]
     bk = contractions(bt)
-    assert len(bk) % 3 == 0 and bk[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"]
+    # grad_x: 2 output tiles over 2000 vocabulary entries (too few for its own K
+    # split), so its work runs as K pieces after an idle main launch
+    assert bk == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x", "tail_pieces", "tail_fixup"], bk
     assert all(ms >= 0 for _, ms in ft.durations() + bt.durations())
 
 
@@ -354,7 +356,9 @@ def test_grad_w_balanced(gpu, dtype, V):
     gx, gW = gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.8], device="cuda"), "sum", timer=bt)
     torch.cuda.synchronize()
     seq = contractions(bt)
-    assert seq[:3] == ["bwd_dlogits", "bwd_grad_w", "bwd_grad_x"], seq
+    # (the dlogit launch of 3 x 32 tiles, K = 2304, runs as K pieces)
+    i = seq.index("bwd_grad_w")
+    assert seq[i + 1] == "bwd_grad_x", seq
     # the same bits again (the shared tiles' sums do not depend on timing)
     gx2, gW2 = gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([0.8], device="cuda"), "sum")
     torch.cuda.synchronize()
@@ -409,6 +413,28 @@ def test_grad_x_balanced(gpu, dtype, panels):
     assert all(b != "tail_pieces" for a, b in zip(seq, seq[1:]) if a == "bwd_grad_x"), seq
     if panels > 1:
         assert seq[:2] == ["bwd_dlogits", "bwd_grad_w"] and seq[2] != "tail_pieces", seq
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_few_tile_launches(gpu, dtype, reduction):
+    """Launches of at most 128 tiles with at least 1024 entries of K run as K pieces
+    only, so the idle CUs share their work: the dlogit launch (4 token x 12
+    vocabulary tiles, K = H = 1536; targets in the first, a middle and the last,
+    ragged vocabulary tile), grad_W (12 x 6 tiles, K = 1024 tokens) and grad_x
+    (4 x 6 tiles, K = 3000 vocabulary entries, one panel: no K split of its own)
+    each run an idle main launch, their pieces and the fixup."""
+    N, H, V = 1024, 1536, 3000
+    x, W, t = make_inputs(N, H, V, dtype, seed=75)
+    t[:5] = [0, 1500, V - 1, 2816, 255]
+    got = check_case(gpu, N, H, V, dtype, reduction, seed=75, grad_loss=1.7, t=t)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(32)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.7], device="cuda"), reduction, timer=bt)
+    torch.cuda.synchronize()
+    seq = contractions(bt)
+    assert seq == ["bwd_dlogits", "tail_pieces", "tail_fixup", "bwd_grad_w", "tail_pieces", "tail_fixup",
+                   "bwd_grad_x", "tail_pieces", "tail_fixup"], seq
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
