@@ -44,6 +44,10 @@ def parse():
                          "uses the largest dlogit panels whose plan fits)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), to scale the HBM counters")
+    ap.add_argument("--dma-calibration", action="store_true",
+                    help="only run the forward on one 256 x 256 tile with H = 65536 (3 times): one workgroup "
+                         "reads x and W (32 MiB each) once through the global -> LDS copies, to check that the "
+                         "counters scaled by the copy calibration count those copies' bytes")
     return ap.parse_args()
 
 
@@ -85,6 +89,22 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def dma_calibration():
+    import torch
+
+    from lm_head_linear_tiled_amd import binding
+    N, H, V = 256, 65536, 256
+    g = torch.Generator(device="cpu").manual_seed(0)
+    x = torch.randn(N, H, generator=g).to(torch.bfloat16).cuda()
+    W = (torch.randn(V, H, generator=g) / 256).to(torch.bfloat16).cuda()
+    t = torch.randint(0, V, (N,), generator=g).cuda()
+    for _ in range(3):
+        binding.flce_forward(x, W, t, "mean")
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "fwd_partial", "compulsory_bytes_read": 2 * N * H * 2 + 8 * N, "launches": 3}),
+          flush=True)
 
 
 def cpu_baseline(x, W, t, dtype, H, V, target_s):
@@ -138,6 +158,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.dma_calibration:
+        dma_calibration()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path has no multi-GPU sharding)",
