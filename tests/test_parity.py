@@ -416,6 +416,29 @@ def test_grad_x_balanced(gpu, dtype, panels):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("panels", [1, 3])
+def test_grad_x_tail_split(gpu, dtype, panels):
+    """A grad_x launch of 16 token x 17 hidden tiles = 272 tiles on 256
+    workgroups: 272 % 256 = 16 is not a multiple of 256 / 8, so the launch is not
+    balanced; the 16 tiles of its partial last round are cut along K (vocabulary)
+    into pieces.  With three vocabulary panels (V = 20000 fp32 / 40000 bf16) grad_x
+    runs once per pair of panels: the second launch's pieces are added to the
+    first's float32 sums and written in the output type."""
+    N, H = 4000, 4352
+    V = 3000 if panels == 1 else (20000 if dtype == "f32" else 40000)
+    got = check_case(gpu, N, H, V, dtype, "mean", seed=72, grad_loss=1.3)
+    x, W, t = make_inputs(N, H, V, dtype, seed=72)
+    xd, Wd, td = to_dev(x, dtype), to_dev(W, dtype), torch.from_numpy(t).cuda()
+    bt = gpu.KernelTimer(256)
+    gpu.flce_backward(xd, Wd, td, got["raw"]["lse"], torch.tensor([1.3], device="cuda"), "mean", timer=bt)
+    torch.cuda.synchronize()
+    seq = contractions(bt)
+    after_gx = [seq[i + 1:i + 3] for i, k in enumerate(seq) if k == "bwd_grad_x"]
+    assert len(after_gx) == (1 if panels == 1 else 2), seq
+    assert all(a == ["tail_pieces", "tail_fixup"] for a in after_gx), seq
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("reduction", ["mean", "sum"])
 def test_few_tile_launches(gpu, dtype, reduction):
     """Launches of at most 128 tiles with at least 1024 entries of K run as K pieces
