@@ -160,7 +160,12 @@ size_t flce_backward_min_workspace_bytes(int64_t N, int64_t H, int64_t V, flce_d
  * atomic accumulation, every sum in a fixed order (of a tile whose K range two
  * workgroups share, the one taking the head of the range starts from the
  * other's partial sums, handed over through the workspace behind a flag), so
- * repeated calls on one device give identical bits.
+ * repeated calls on one device give identical bits.  The hand-over waits for a
+ * workgroup of the same launch; with one or two launches of this kind running
+ * on a GPU at once the wait always ends.  Should so many run concurrently (from
+ * other streams or processes) that their waiting workgroups hold every CU, the
+ * wait gives up after about a second of polling and those tiles' gradients are
+ * wrong; callers that share a GPU that widely should not overlap backward calls.
  */
 flce_status flce_backward(const void* x, const void* W, const int64_t* target,
                           const float* lse, const float* grad_loss, int64_t N, int64_t H,
