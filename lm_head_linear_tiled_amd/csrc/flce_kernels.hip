@@ -562,23 +562,33 @@ __device__ __forceinline__ void staged_epilogue(char* spare, Val&& val, Out&& ou
     };
 #pragma unroll
     for (int jj = 0; jj < JR; ++jj) fix(rd * JR + jj, jj * 32, poke);
-    // read back whole output rows of one wave's region and store them
+    // read back whole output rows of one wave's region and store them, NB reads
+    // issued before their stores (the stores are predicated on the output
+    // bounds, and a read behind such a branch waits for the one before it); the
+    // paired drain of the dlogit store waves keeps one read in flight (its
+    // kernel has no registers to spare)
     auto drain = [&](const char* src_sc, auto&& put) {
+      constexpr int NB = PAIRW == 0 ? 8 : 1;
+      constexpr int RQ = BF ? 8 : 4;  // rows per read
+      const int k = BF ? (l & 7) : (l & 15);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        int row, k;
-        uint4 v;
-        if constexpr (BF) {
-          row = q * 8 + (l >> 3);
-          k = l & 7;
-          v = *reinterpret_cast<const uint4*>(src_sc + row * RB + ((k ^ ((row >> 1) & 7)) * 16));
-          if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        } else {
-          row = q * 4 + (l >> 4);
-          k = l & 15;
-          v = *reinterpret_cast<const uint4*>(src_sc + row * RB + ((k ^ (row & 15)) * 16));
+      for (int q0 = 0; q0 < 8; q0 += NB) {
+        uint4 v[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int row = (q0 + q) * RQ + l / (64 / RQ);
+          const int slot = BF ? (k ^ ((row >> 1) & 7)) : (k ^ (row & 15));
+          v[q] = *reinterpret_cast<const uint4*>(src_sc + row * RB + slot * 16);
         }
-        put(rd * TR + row, k * (16 / (int)sizeof(S)), v);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int row = (q0 + q) * RQ + l / (64 / RQ);
+          // the halves were swapped in rows with bit 4 set: (q0 + q) / 2 odd, as
+          // l / 8 < 8
+          if constexpr (BF)
+            if (((q0 + q) >> 1) & 1) v[q] = make_uint4(v[q].z, v[q].w, v[q].x, v[q].y);
+          put(rd * TR + row, k * (16 / (int)sizeof(S)), v[q]);
+        }
       }
     };
     if constexpr (PAIRW == 0) {
@@ -843,10 +853,15 @@ __global__ __launch_bounds__(256) void dlogit_tail_fixup(const float* __restrict
 }
 
 // Output of a backward contraction through the staged epilogue: out rows are
-// the N side of the tile (row_ok tells which exist and row_off gives their
-// element offset), M (hidden) is contiguous.  final: write T to dst, else the
-// float32 partial sums to acc_buf (the sums of earlier launches are already in
-// acc, see grad_init); a final tile stages T directly.
+// the N side of the tile (row_ok tells which exist, a prefix of them, and
+// row_off gives their element offset, linear in the row), M (hidden) is
+// contiguous.  final: write T to dst, else the float32 partial sums to acc_buf
+// (the sums of earlier launches are already in acc, see grad_init); a final
+// tile stages T directly.  The stores are buffer stores from the wave's first
+// output element: rows past the last existing one fall outside the buffer's
+// range and hidden entries >= H get an offset outside it, so no store is
+// predicated (no branch, 32-bit offsets; a row spans at most 16 MiB, so the 128
+// rows of a wave stay below 2^31 bytes).
 template <typename T, class G, class RowOk, class RowOff>
 __device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare, int hw, int nw, int H, int final,
                                               T* __restrict__ dst, float* __restrict__ acc_buf, RowOk&& row_ok,
@@ -855,17 +870,32 @@ __device__ __forceinline__ void grad_epilogue(typename G::Acc& acc, char* spare,
 #pragma unroll
     for (int u = 0; u < 4; ++u) d[u] = acc[i][j][4 * g + u];
   };
-  if (final) {
-    staged_epilogue<T, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
-      if (!row_ok(nw + n) || hw + m >= H) return;
-      *reinterpret_cast<uint4*>(dst + row_off(nw + n) + hw + m) = v;
-    });
-  } else {
-    staged_epilogue<float, G::FM, G::FN>(spare, val, [&](int n, int m, uint4 v) {
-      if (!row_ok(nw + n) || hw + m >= H) return;
-      *reinterpret_cast<uint4*>(acc_buf + row_off(nw + n) + hw + m) = v;
-    });
+  hw = __builtin_amdgcn_readfirstlane(hw);
+  nw = __builtin_amdgcn_readfirstlane(nw);
+  int nv = 0, hi = G::FN * 32;  // rows < nv exist, rows >= hi do not
+  while (nv < hi) {
+    const int mid = (nv + hi) >> 1;
+    if (row_ok(nw + mid))
+      nv = mid + 1;
+    else
+      hi = mid;
   }
+  const int64_t o0 = row_off(nw);
+  const uint32_t ld = (uint32_t)(row_off(nw + 1) - o0);
+  auto store = [&](auto* base) {
+    constexpr uint32_t ES = sizeof(*base);
+    const uint64_t bytes = (uint64_t)nv * ld * ES;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + o0 + hw), (short)0, (uint32_t)(bytes < 0x80000000ull ? bytes : 0x80000000ull), 0x00020000);
+    return [=](int n, int m, uint4 v) {
+      const uint32_t off = hw + m < H ? ((uint32_t)n * ld + (uint32_t)m) * ES : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+    };
+  };
+  if (final)
+    staged_epilogue<T, G::FM, G::FN>(spare, val, store(dst));
+  else
+    staged_epilogue<float, G::FM, G::FN>(spare, val, store(acc_buf));
 }
 
 // Start of a gradient tile: zero, or, when the output is summed over several
@@ -1578,3 +1608,20 @@ hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* 
 }
 
 }  // namespace flce
+
+#if FLCE_TILE_CLOCK
+// Measurement builds: copy the tile clock records (2 x 256 x 64 x 5 64-bit
+// values, see gemm_core.h) to host memory `dst` (at most `bytes`), or clear
+// them; synchronous, on the current device.  hipError_t codes.
+extern "C" int flce_tile_clock_read(void* dst, size_t bytes) {
+  const size_t n = bytes < sizeof(flce::tile_clock) ? bytes : sizeof(flce::tile_clock);
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(flce::tile_clock), n, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int flce_tile_clock_clear() {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(flce::tile_clock));
+  if (e == hipSuccess) e = hipMemset(p, 0, sizeof(flce::tile_clock));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return (int)e;
+}
+#endif

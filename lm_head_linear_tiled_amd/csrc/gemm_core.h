@@ -47,6 +47,19 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 enum Major { K_MAJOR = 0, MN_MAJOR = 1 };
 
+// Measurement builds only (FLCE_TILE_CLOCK=1): the register-staged kernels (the
+// gradient contractions) record, for workgroup b < 256 and its items j < 64, the
+// shader clock (s_memtime) at the start of the item's first K slice, after that
+// slice, after its last slice and after its epilogue, and its slice count, in
+// tile_clock[kind][b][j]; kind 0: both operands MN-major, 1: B K-major.  Every
+// launch overwrites the entries of the items it runs.
+#ifndef FLCE_TILE_CLOCK
+#define FLCE_TILE_CLOCK 0
+#endif
+#if FLCE_TILE_CLOCK
+__device__ unsigned long long tile_clock[2][256][64][5];
+#endif
+
 #ifndef FLCE_COPY_STEPS
 #define FLCE_COPY_STEPS 0
 #endif
@@ -690,9 +703,20 @@ struct TileGemm {
       call_init(init, acc, tm0, tn0, tkb, tkt);
     else
       init(acc, tm0, tn0);
+    // tile clock (measurement builds): item jj, field f
+    auto stamp = [&](int jj, int f, unsigned long long v) {
+#if FLCE_TILE_CLOCK
+      if constexpr (STAGING == STAGE_REG)
+        if (threadIdx.x == 0 && blockIdx.x < 256 && jj < 64) tile_clock[BMAJ == MN_MAJOR ? 0 : 1][blockIdx.x][jj][f] = v;
+#endif
+    };
     int q = 0;
     for (int j = 0;;) {
       const int nkt = SEG ? tkt : KT;
+      if constexpr (FLCE_TILE_CLOCK != 0) {
+        stamp(j, 0, __builtin_amdgcn_s_memtime());
+        stamp(j, 4, (unsigned long long)nkt);
+      }
       for (int kt = 0; kt < nkt; ++kt, ++q) {
         // After an epilogue only LDS work is drained: every wave waited for its
         // copies of this slice before the epilogue, so the global stores the
@@ -710,7 +734,10 @@ struct TileGemm {
         else
           slice<LEAN, false>(A, B, lds, q & 1, pm0, pn0, pk0, acc);
         advance();
+        if constexpr (FLCE_TILE_CLOCK != 0)
+          if (kt == 0) stamp(j, 1, __builtin_amdgcn_s_memtime());
       }
+      if constexpr (FLCE_TILE_CLOCK != 0) stamp(j, 2, __builtin_amdgcn_s_memtime());
       // this wave's copies of the next tile's first slice have landed (a wave
       // without copies leaves its stores in flight)
       if (cw) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -718,6 +745,7 @@ struct TileGemm {
         call_epi(epi, acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES, tkb, tkt);
       else
         epi(acc, tm0, tn0, (char*)lds + ((q - 1) & 1) * STAGE_BYTES);
+      if constexpr (FLCE_TILE_CLOCK != 0) stamp(j, 3, __builtin_amdgcn_s_memtime());
       if (!next_tile(next, ++j, tm0, tn0, tkb, tkt)) break;
       if constexpr (SEG)
         call_init(init, acc, tm0, tn0, tkb, tkt);
