@@ -25,6 +25,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_default_build_has_no_tile_clock(lib):
+    """The tile clock exists only in measurement builds (FLCE_TILE_CLOCK=1)."""
+    assert not hasattr(lib, "flce_tile_clock_read") and not hasattr(lib, "flce_tile_clock_clear")
+
+
+def test_bench_tile_clock_needs_a_clock_build():
+    """bench.py --tile-clock refuses to run without --lib, and with a library that
+    has no tile clock (the default build), before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for extra, msg in (([], "needs --lib"), (["--lib", binding.LIB_PATH], "was not built with FLCE_TILE_CLOCK")):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--tile-clock", *extra],
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode != 0 and msg in r.stderr, (r.returncode, r.stderr[-500:])
+
+
 def test_status_strings(lib):
     for code in range(10):
         s = binding.status_string(code)
