@@ -49,10 +49,10 @@ def parse():
                          "reads x and W (32 MiB each) once through the global -> LDS copies, to check that the "
                          "counters scaled by the copy calibration count those copies' bytes")
     ap.add_argument("--tile-clock", action="store_true",
-                    help="only report where the gradient kernels' cycles go, per output tile (first K slice, "
-                         "steady K slices, epilogue, gap to the next tile) at N = 4096 and 2048, H = 4096, "
-                         "V = 32768, bf16 (launches without split tails); needs --lib with a build made with "
-                         "--define FLCE_TILE_CLOCK=1")
+                    help="only report where the forward's and the backward kernels' cycles go, per output "
+                         "tile (first K slice, steady K slices, epilogue, gap to the next tile) at N = 4096 and "
+                         "2048, H = 4096, V = 32768, bf16 (launches without split tails); needs --lib with a build "
+                         "made with --define FLCE_TILE_CLOCK=1")
     return ap.parse_args()
 
 
@@ -113,9 +113,10 @@ def dma_calibration():
 
 
 def tile_clock(lib_path):
-    """Per-tile cycle split of the last grad_W and grad_x launches of one backward
-    (a build with FLCE_TILE_CLOCK records the shader clock at each item's start,
-    after its first K slice, after its last K slice and after its epilogue)."""
+    """Per-tile cycle split of the forward and of the last dlogit, grad_W and grad_x
+    launches of one backward (a build with FLCE_TILE_CLOCK records the shader clock
+    at each item's start, after its first K slice, after its last K slice and after
+    its epilogue)."""
     import ctypes
 
     import numpy as np
@@ -133,46 +134,55 @@ def tile_clock(lib_path):
     lib.flce_tile_clock_read.restype = ctypes.c_int
     lib.flce_tile_clock_clear.argtypes = []
     lib.flce_tile_clock_clear.restype = ctypes.c_int
-    rec = np.zeros((2, 256, 64, 5), np.uint64)
+    rec = np.zeros((4, 256, 64, 5), np.uint64)
     ideal = 256 * 256 * 64 * 2 / 4096  # cycles of one bf16 K slice at the CU's MFMA peak (4096 flop/clock)
+
+    def report(kind, name, N, H, V):
+        r = rec[kind].astype(np.int64)
+        items, gaps = [], []
+        for b in range(256):
+            for j in range(64):
+                if r[b, j, 3] == 0:
+                    continue
+                nkt = int(r[b, j, 4])
+                items.append((nkt, r[b, j, 1] - r[b, j, 0], (r[b, j, 2] - r[b, j, 1]) / max(nkt - 1, 1),
+                              r[b, j, 3] - r[b, j, 2]))
+                if j + 1 < 64 and r[b, j + 1, 3] != 0:
+                    gaps.append(r[b, j + 1, 0] - r[b, j, 3])
+        a = np.array(items, dtype=np.float64)
+        nkt = float(np.median(a[:, 0]))
+        first, steady, epi = (float(np.median(a[:, c])) for c in (1, 2, 3))
+        gap = float(np.median(gaps)) if gaps else 0.0
+        tile = first + (nkt - 1) * steady + epi + gap
+        print(json.dumps({"kernel": name, "N": N, "H": H, "V": V, "items": len(items),
+                          "items_per_workgroup": round(len(items) / 256, 2), "k_slices": nkt,
+                          "first_slice": first, "steady_slice": round(steady, 1), "epilogue": epi,
+                          "gap": gap if gaps else None, "ideal_slice": ideal,
+                          "steady_mfma_frac": round(ideal / steady, 4),
+                          "tile_mfma_frac": round(nkt * ideal / tile, 4),
+                          "unit": "shader clock cycles (medians over items)"}), flush=True)
+
     for N, H, V in ((4096, 4096, 32768), (2048, 4096, 32768)):
         x, W, t = make_inputs(N, H, V, "bf16", seed=0)
         xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
         Wd = torch.from_numpy(W.view(np.int16)).view(torch.bfloat16).cuda()
         td = torch.from_numpy(t).cuda()
         gl = torch.ones(1, dtype=torch.float32, device="cuda")
-        _, lse = binding.flce_forward(xd, Wd, td, "mean")
         for _ in range(3):
+            _, lse = binding.flce_forward(xd, Wd, td, "mean")
             binding.flce_backward(xd, Wd, td, lse, gl, "mean")
         torch.cuda.synchronize()
+        assert lib.flce_tile_clock_clear() == 0
+        binding.flce_forward(xd, Wd, td, "mean")
+        torch.cuda.synchronize()
+        assert lib.flce_tile_clock_read(rec.ctypes.data, rec.nbytes) == 0
+        report(3, "fwd_partial", N, H, V)
         assert lib.flce_tile_clock_clear() == 0
         binding.flce_backward(xd, Wd, td, lse, gl, "mean")
         torch.cuda.synchronize()
         assert lib.flce_tile_clock_read(rec.ctypes.data, rec.nbytes) == 0
-        for kind, name in ((0, "bwd_grad_w"), (1, "bwd_grad_x")):
-            r = rec[kind].astype(np.int64)
-            items, gaps = [], []
-            for b in range(256):
-                for j in range(64):
-                    if r[b, j, 3] == 0:
-                        continue
-                    nkt = int(r[b, j, 4])
-                    items.append((nkt, r[b, j, 1] - r[b, j, 0], (r[b, j, 2] - r[b, j, 1]) / max(nkt - 1, 1),
-                                  r[b, j, 3] - r[b, j, 2]))
-                    if j + 1 < 64 and r[b, j + 1, 3] != 0:
-                        gaps.append(r[b, j + 1, 0] - r[b, j, 3])
-            a = np.array(items, dtype=np.float64)
-            nkt = float(np.median(a[:, 0]))
-            first, steady, epi = (float(np.median(a[:, c])) for c in (1, 2, 3))
-            gap = float(np.median(gaps)) if gaps else 0.0
-            tile = first + (nkt - 1) * steady + epi + (gap if gaps else 0.0)
-            print(json.dumps({"kernel": name, "N": N, "H": H, "V": V, "items": len(items),
-                              "items_per_workgroup": round(len(items) / 256, 2), "k_slices": nkt,
-                              "first_slice": first, "steady_slice": round(steady, 1), "epilogue": epi,
-                              "gap": gap if gaps else None, "ideal_slice": ideal,
-                              "steady_mfma_frac": round(ideal / steady, 4),
-                              "tile_mfma_frac": round(nkt * ideal / tile, 4),
-                              "unit": "shader clock cycles (medians over items)"}), flush=True)
+        for kind, name in ((2, "bwd_dlogits"), (0, "bwd_grad_w"), (1, "bwd_grad_x")):
+            report(kind, name, N, H, V)
 
 
 def cpu_baseline(x, W, t, dtype, H, V, target_s):

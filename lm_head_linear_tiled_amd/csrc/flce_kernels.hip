@@ -1610,7 +1610,7 @@ hipError_t launch_backward(int dt, const BwdPlan& p, const void* x, const void* 
 }  // namespace flce
 
 #if FLCE_TILE_CLOCK
-// Measurement builds: copy the tile clock records (2 x 256 x 64 x 5 64-bit
+// Measurement builds: copy the tile clock records (4 x 256 x 64 x 5 64-bit
 // values, see gemm_core.h) to host memory `dst` (at most `bytes`), or clear
 // them; synchronous, on the current device.  hipError_t codes.
 extern "C" int flce_tile_clock_read(void* dst, size_t bytes) {

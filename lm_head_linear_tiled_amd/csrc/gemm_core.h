@@ -47,17 +47,21 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 enum Major { K_MAJOR = 0, MN_MAJOR = 1 };
 
-// Measurement builds only (FLCE_TILE_CLOCK=1): the register-staged kernels (the
-// gradient contractions) record, for workgroup b < 256 and its items j < 64, the
-// shader clock (s_memtime) at the start of the item's first K slice, after that
-// slice, after its last slice and after its epilogue, and its slice count, in
-// tile_clock[kind][b][j]; kind 0: both operands MN-major, 1: B K-major.  Every
-// launch overwrites the entries of the items it runs.
+// Measurement builds only (FLCE_TILE_CLOCK=1): every persistent tile loop
+// records, for workgroup b < 256 and its items j < 64, the shader clock
+// (s_memtime, a per-CU counter: only differences within a workgroup mean
+// anything) at the start of the item's first K slice, after that slice, after
+// its last slice and after its epilogue, and its slice count, in
+// tile_clock[kind][b][j]; kind 0: register-staged with both operands MN-major
+// (grad_W), 1: register-staged with B K-major (grad_x), 2: DMA copies by copy
+// waves with separate store waves (dlogits), 3: other DMA kernels (the forward,
+// the dlogit tail pieces).  Every launch overwrites the entries of the items it
+// runs.
 #ifndef FLCE_TILE_CLOCK
 #define FLCE_TILE_CLOCK 0
 #endif
 #if FLCE_TILE_CLOCK
-__device__ unsigned long long tile_clock[2][256][64][5];
+__device__ unsigned long long tile_clock[4][256][64][5];
 #endif
 
 #ifndef FLCE_COPY_STEPS
@@ -706,8 +710,8 @@ struct TileGemm {
     // tile clock (measurement builds): item jj, field f
     auto stamp = [&](int jj, int f, unsigned long long v) {
 #if FLCE_TILE_CLOCK
-      if constexpr (STAGING == STAGE_REG)
-        if (threadIdx.x == 0 && blockIdx.x < 256 && jj < 64) tile_clock[BMAJ == MN_MAJOR ? 0 : 1][blockIdx.x][jj][f] = v;
+      constexpr int KIND = STAGING == STAGE_REG ? (BMAJ == MN_MAJOR ? 0 : 1) : (SPLIT ? 2 : 3);
+      if (threadIdx.x == 0 && blockIdx.x < 256 && jj < 64) tile_clock[KIND][blockIdx.x][jj][f] = v;
 #endif
     };
     int q = 0;
